@@ -1,0 +1,321 @@
+"""CPU fp64 oracle for the DPO sequence log-probability, loss and LM-head gradient.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with
+the HIP path and imports nothing from it; the only thing both sides share is
+the seeded input generator, which holds none of the arithmetic below.
+
+What is computed, and where the pages define it
+-----------------------------------------------
+"DPO Training on GPU, in depth" (aicassindra.com):
+  * section "What one DPO step computes": the loss is minus the log-sigmoid
+    of beta times the difference between the chosen and rejected
+    policy-minus-reference log-ratios; sequence scores are sums of token
+    log-probabilities over completion tokens only; chosen and rejected rows
+    are concatenated into one batch of 2B rows.
+  * section "A worked example of the numbers": implicit reward = beta times
+    the log-ratio, margin = chosen reward minus rejected reward, the
+    per-pair gradient is scaled by sigmoid(-margin), and a policy equal to the
+    reference gives loss ln 2.
+  * section "A training configuration that fits" (the hand-written chunked
+    loss): fp32-or-better log-softmax over the whole vocabulary, gather of
+    the target token, masked sum per row, mean of the per-pair loss over
+    pairs, accuracy = fraction of pairs with margin strictly above zero.
+"Run Distributed Full-Model DPO with PyTorch FSDP" (aimastery.page), section
+"Step 4: Computing Concatenated Forward Passes": chosen rows first, then
+rejected rows, split at half the batch, summed (not averaged) log-probs.
+"feat(training): add DPO training with offline-scored reference model",
+changelog and section "Why the reference is scored offline": chosen and
+rejected rows of a pair sit next to each other; reference scores are plain
+per-row sums with no beta.
+
+Readings taken where the pages leave a step open (all listed in the design doc):
+targets arrive already shifted (targets[r, t] is the token predicted from
+hidden[r, t]); an explicit 0/1 mask selects completion positions and targets
+at mask-0 positions are never read; accuracy uses a strict ``>``; the
+gradient weight of a row is w = -d loss / d score = +-beta*sigmoid(-m)/B.
+
+Everything is float64.  bf16 inputs are widened exactly (bits << 16).  The
+LM-head contraction uses numpy's BLAS matmul in float64 as a library step.
+Every function here is pinned by tests in tests/test_oracle_pins.py against
+the worked example, closed forms, brute force, finite differences and a
+PyTorch-fp64 autograd cross-check.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Tuple
+
+import numpy as np
+
+PAIRS_ADJACENT = 0
+PAIRS_HALVES = 1
+
+
+# ----------------------------------------------------------------------------
+# input decoding
+# ----------------------------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns: the 16 bits are the top half of a float32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even); returns float64 values.
+
+    Used only to state the expected value of a bf16 output.  Implemented by
+    scaling to the bf16 grid of each value's binade: a bf16 number has 8
+    significant bits, so the spacing in [2^e, 2^(e+1)) is 2^(e-7).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    nz = x != 0
+    e = np.floor(np.log2(np.abs(x[nz])))
+    # guard log2 rounding at exact powers of two
+    e = np.where(np.abs(x[nz]) < 2.0 ** e, e - 1, e)
+    e = np.where(np.abs(x[nz]) >= 2.0 ** (e + 1), e + 1, e)
+    ulp = 2.0 ** (e - 7)
+    out[nz] = np.round(x[nz] / ulp) * ulp  # numpy rounds half to even
+    return out
+
+
+# ----------------------------------------------------------------------------
+# completion positions ("sums run only over completion tokens")
+# ----------------------------------------------------------------------------
+def completion_positions(mask: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Flat indices r*T+t of completion positions in row-major order, and per-row counts."""
+    m = np.asarray(mask) != 0
+    idx = np.flatnonzero(m.reshape(-1)).astype(np.int64)
+    n_tokens = m.sum(axis=1).astype(np.int64)
+    return idx, n_tokens
+
+
+def _check_targets(targets_at_idx: np.ndarray, V: int) -> None:
+    if targets_at_idx.size and (targets_at_idx.min() < 0 or targets_at_idx.max() >= V):
+        raise ValueError("target id out of range at a completion position")
+
+
+# ----------------------------------------------------------------------------
+# per-position log-softmax over the whole vocabulary and target gather
+# ----------------------------------------------------------------------------
+def logsumexp_rows(Z: np.ndarray) -> np.ndarray:
+    """log(sum_v exp(Z[i, v])) per row, shifted by the row max for range safety."""
+    m = Z.max(axis=1)
+    return m + np.log(np.exp(Z - m[:, None]).sum(axis=1))
+
+
+def position_logps(Z: np.ndarray, tgt: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """(lse, log p(target)) for each row of a logits block Z [n, V]."""
+    lse = logsumexp_rows(Z)
+    return lse, Z[np.arange(Z.shape[0]), tgt] - lse
+
+
+def _row_sums(logp_flat: np.ndarray, idx: np.ndarray, R: int, T: int) -> np.ndarray:
+    """Exactly rounded per-row sum of the per-position log-probs (math.fsum)."""
+    sums = np.zeros(R, dtype=np.float64)
+    rows = idx // T
+    for r in range(R):
+        sums[r] = math.fsum(logp_flat[idx[rows == r]].tolist())
+    return sums
+
+
+def seq_logps_f64(hidden: np.ndarray, w: np.ndarray, targets: np.ndarray, mask: np.ndarray,
+                  chunk: int = 256) -> Dict[str, np.ndarray]:
+    """Sequence scores from hidden states [R,T,H] (float64) and W_vocab [V,H] (float64).
+
+    Returns logp_sum [R] (exact sums), lse [R,T] and logp [R,T] (0 at mask-0
+    positions), n_tokens [R], idx [N_c].
+    """
+    R, T, H = hidden.shape
+    V = w.shape[0]
+    idx, n_tokens = completion_positions(mask)
+    tflat = np.asarray(targets).reshape(-1).astype(np.int64)
+    _check_targets(tflat[idx], V)
+    hflat = hidden.reshape(R * T, H)
+    lse = np.zeros(R * T)
+    logp = np.zeros(R * T)
+    for s in range(0, idx.size, chunk):
+        c = idx[s:s + chunk]
+        Z = hflat[c] @ w.T
+        lse[c], logp[c] = position_logps(Z, tflat[c])
+    return dict(logp_sum=_row_sums(logp, idx, R, T), lse=lse.reshape(R, T),
+                logp=logp.reshape(R, T), n_tokens=n_tokens, idx=idx)
+
+
+def seq_logps(hidden_bits, w_bits, targets, mask, chunk: int = 256) -> Dict[str, np.ndarray]:
+    """As ``seq_logps_f64`` on bf16 bit-pattern inputs."""
+    return seq_logps_f64(bf16_to_f64(hidden_bits), bf16_to_f64(w_bits), targets, mask, chunk)
+
+
+def logits_seq_logps_f64(logits: np.ndarray, targets: np.ndarray, mask: np.ndarray,
+                         chunk: int = 256) -> Dict[str, np.ndarray]:
+    """Sequence scores from given logits [R,T,V] (float64)."""
+    R, T, V = logits.shape
+    idx, n_tokens = completion_positions(mask)
+    tflat = np.asarray(targets).reshape(-1).astype(np.int64)
+    _check_targets(tflat[idx], V)
+    lflat = logits.reshape(R * T, V)
+    lse = np.zeros(R * T)
+    logp = np.zeros(R * T)
+    for s in range(0, idx.size, chunk):
+        c = idx[s:s + chunk]
+        lse[c], logp[c] = position_logps(lflat[c], tflat[c])
+    return dict(logp_sum=_row_sums(logp, idx, R, T), lse=lse.reshape(R, T),
+                logp=logp.reshape(R, T), n_tokens=n_tokens, idx=idx)
+
+
+def logits_seq_logps(logits_bits, targets, mask, chunk: int = 256) -> Dict[str, np.ndarray]:
+    """As ``logits_seq_logps_f64`` on bf16 bit patterns, decoded chunk by chunk."""
+    R, T, V = logits_bits.shape
+    idx, n_tokens = completion_positions(mask)
+    tflat = np.asarray(targets).reshape(-1).astype(np.int64)
+    _check_targets(tflat[idx], V)
+    lflat = logits_bits.reshape(R * T, V)
+    lse = np.zeros(R * T)
+    logp = np.zeros(R * T)
+    for s in range(0, idx.size, chunk):
+        c = idx[s:s + chunk]
+        lse[c], logp[c] = position_logps(bf16_to_f64(lflat[c]), tflat[c])
+    return dict(logp_sum=_row_sums(logp, idx, R, T), lse=lse.reshape(R, T),
+                logp=logp.reshape(R, T), n_tokens=n_tokens, idx=idx)
+
+
+# ----------------------------------------------------------------------------
+# the sigmoid DPO loss
+# ----------------------------------------------------------------------------
+def pair_rows(num_pairs: int, layout: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Chosen and rejected row indices of each pair."""
+    i = np.arange(num_pairs)
+    if layout == PAIRS_ADJACENT:
+        return 2 * i, 2 * i + 1
+    if layout == PAIRS_HALVES:
+        return i, num_pairs + i
+    raise ValueError("unknown pair layout")
+
+
+def softplus(x: np.ndarray) -> np.ndarray:
+    """log(1 + exp(x)) without overflow: max(x, 0) + log1p(exp(-|x|))."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """1 / (1 + exp(-x)), evaluated on the side that cannot overflow."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def dpo_loss(policy_sum: np.ndarray, ref_sum: np.ndarray, beta: float,
+             layout: int = PAIRS_ADJACENT) -> Dict[str, np.ndarray]:
+    """Sigmoid DPO loss over pairs of rows.
+
+    margin_i = beta*((pi_c - ref_c) - (pi_r - ref_r)); loss = mean_i -log sigmoid(margin_i)
+    = mean_i softplus(-margin_i).  weight = -d loss / d pi per row:
+    +beta*sigmoid(-margin_i)/B on the chosen row, the negative on the rejected row.
+    reward = beta*(pi - ref) per row; accuracy = mean(margin_i > 0).
+    """
+    if not (np.isfinite(beta) and beta > 0):
+        raise ValueError("beta must be finite and positive")
+    pi = np.asarray(policy_sum, dtype=np.float64)
+    ref = np.asarray(ref_sum, dtype=np.float64)
+    R = pi.size
+    if R % 2 or R == 0:
+        raise ValueError("rows must be even and positive")
+    B = R // 2
+    c, r = pair_rows(B, layout)
+    reward = beta * (pi - ref)
+    margin = reward[c] - reward[r]
+    loss = float(np.mean(softplus(-margin)))
+    s = sigmoid(-margin)
+    weight = np.zeros(R)
+    weight[c] = beta * s / B
+    weight[r] = -beta * s / B
+    return dict(loss=loss, weight=weight, reward=reward, margin=margin,
+                accuracy=float(np.mean(margin > 0)), sig_neg_margin=s)
+
+
+# ----------------------------------------------------------------------------
+# backward: dlogits = w * (softmax - onehot), dHidden = D @ W, dW = D^T @ Hc
+# ----------------------------------------------------------------------------
+def _row_weight(weight: np.ndarray, idx: np.ndarray, T: int) -> np.ndarray:
+    return np.asarray(weight, dtype=np.float64)[idx // T]
+
+
+def head_backward_f64(hidden: np.ndarray, w: np.ndarray, targets: np.ndarray, mask: np.ndarray,
+                      lse: np.ndarray, weight: np.ndarray, chunk: int = 256
+                      ) -> Tuple[np.ndarray, np.ndarray]:
+    """Gradient of the loss w.r.t. hidden [R,T,H] and W_vocab [V,H].
+
+    ``weight`` is -d loss / d score per row; ``lse`` the per-position
+    log-sum-exp from the forward.  For a completion position t with target y:
+    d loss / d z[t, v] = w_r * (softmax(z_t)[v] - [v == y]).  Mask-0 positions
+    get an exactly zero hidden gradient.
+    """
+    R, T, H = hidden.shape
+    V = w.shape[0]
+    idx, _ = completion_positions(mask)
+    tflat = np.asarray(targets).reshape(-1).astype(np.int64)
+    _check_targets(tflat[idx], V)
+    hflat = hidden.reshape(R * T, H)
+    lse_flat = np.asarray(lse, dtype=np.float64).reshape(-1)
+    wrow = _row_weight(weight, idx, T)
+    dH = np.zeros((R * T, H))
+    dW = np.zeros((V, H))
+    for s in range(0, idx.size, chunk):
+        c = idx[s:s + chunk]
+        Hc = hflat[c]
+        Z = Hc @ w.T
+        P = np.exp(Z - lse_flat[c][:, None])
+        P[np.arange(c.size), tflat[c]] -= 1.0
+        D = wrow[s:s + chunk][:, None] * P
+        dH[c] = D @ w
+        dW += D.T @ Hc
+    return dH.reshape(R, T, H), dW
+
+
+def head_backward(hidden_bits, w_bits, targets, mask, lse, weight, chunk: int = 256):
+    """As ``head_backward_f64`` on bf16 bit-pattern inputs."""
+    return head_backward_f64(bf16_to_f64(hidden_bits), bf16_to_f64(w_bits), targets, mask,
+                             lse, weight, chunk)
+
+
+def logits_backward_rows(logits_bits, targets, mask, lse, weight, flat_positions) -> np.ndarray:
+    """dlogits [n, V] (float64) for the given flat positions of a [R,T,V] logits input.
+
+    Completion positions get w_r*(softmax - onehot); mask-0 positions get 0.
+    """
+    R, T, V = logits_bits.shape
+    pos = np.asarray(flat_positions, dtype=np.int64)
+    lflat = logits_bits.reshape(R * T, V)
+    m = np.asarray(mask).reshape(-1) != 0
+    tflat = np.asarray(targets).reshape(-1).astype(np.int64)
+    lse_flat = np.asarray(lse, dtype=np.float64).reshape(-1)
+    out = np.zeros((pos.size, V))
+    live = np.flatnonzero(m[pos])
+    if live.size:
+        p = pos[live]
+        _check_targets(tflat[p], V)
+        P = np.exp(bf16_to_f64(lflat[p]) - lse_flat[p][:, None])
+        P[np.arange(p.size), tflat[p]] -= 1.0
+        out[live] = _row_weight(weight, p, T)[:, None] * P
+    return out
+
+
+# ----------------------------------------------------------------------------
+# the whole path on one batch
+# ----------------------------------------------------------------------------
+def head_step(hidden_bits, w_bits, targets, mask, ref_sum, beta, layout=PAIRS_ADJACENT,
+              chunk: int = 256) -> Dict[str, np.ndarray]:
+    """Forward scores, loss and head gradients for one batch (float64 throughout)."""
+    hidden = bf16_to_f64(hidden_bits)
+    w = bf16_to_f64(w_bits)
+    fwd = seq_logps_f64(hidden, w, targets, mask, chunk)
+    loss = dpo_loss(fwd["logp_sum"], ref_sum, beta, layout)
+    dH, dW = head_backward_f64(hidden, w, targets, mask, fwd["lse"], loss["weight"], chunk)
+    out = dict(fwd)
+    out.update(loss)
+    out["d_hidden"] = dH
+    out["d_w"] = dW
+    return out
