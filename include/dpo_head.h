@@ -1,0 +1,188 @@
+/* dpo_head.h - C ABI of the DPO LM-head log-probability / loss / gradient path
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  "DPO Training on GPU, in depth" (aicassindra.com),
+ * section "What one DPO step computes": each preference pair is a prompt with
+ * a chosen and a rejected completion; a completion's score is the sum of its
+ * token log-probabilities over completion tokens only; the loss is minus the
+ * log-sigmoid of beta times the chosen-minus-rejected difference of
+ * policy-minus-reference scores; chosen and rejected rows are concatenated
+ * into one batch of 2B rows.  Section "A training configuration that fits"
+ * gives the per-token step as a full-vocabulary log-softmax, a gather of the
+ * target token, and a masked fp32-or-better sum per row; its memory section
+ * ("Where the memory goes for an 8B model") is why the fused entry points
+ * never build the [rows x T x V] logits.
+ *
+ * Conventions for every entry point:
+ *  - Array arguments are DEVICE pointers owned by the caller.  The library
+ *    never allocates or frees device memory and keeps no pointer after a call
+ *    returns.  Scratch space is the caller's `workspace`, sized by
+ *    dpo_workspace_bytes().
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
+ *    stream) and is asynchronous: outputs are valid once the stream has
+ *    reached the end of the call.
+ *  - Arguments are validated on the host before anything is enqueued; on
+ *    error nothing is enqueued and a negative DPO_ERR_* code is returned.
+ *  - bf16 arrays hold raw bfloat16 bit patterns (uint16_t).
+ *  - "Aligned" targets: targets[r*T+t] is the token whose probability is read
+ *    from the logits computed at (r, t); the caller applies the one-position
+ *    shift of the page's hand-written loss by slicing.  mask[r*T+t] != 0
+ *    marks a completion position.  Targets at mask-0 positions are never
+ *    read as indices (they may hold the ignore value -100).
+ *  - Shape rules: rows even and > 0; T, H, V > 0; H % 64 == 0; V % 8 == 0;
+ *    rows*T < 2^31.  Pointers to bf16 and float arrays must be 16-byte
+ *    aligned.
+ *  - Target ids outside [0, V) at completion positions are detected on the
+ *    device: the call's outputs for that position are NaN and
+ *    dpo_device_status() reports DPO_ERR_TARGET_RANGE.
+ *  - Results are deterministic run to run: no floating-point atomics.
+ *  - Calls that share a workspace must not overlap in time (same stream, or
+ *    ordered by events).
+ */
+#ifndef DPO_HEAD_H
+#define DPO_HEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t dpo_bf16; /* raw bfloat16 bits */
+
+enum {
+  DPO_OK = 0,
+  DPO_ERR_NULL = -1,         /* a required pointer is NULL */
+  DPO_ERR_SHAPE = -2,        /* a size breaks the shape rules */
+  DPO_ERR_ALIGN = -3,        /* a pointer is not 16-byte aligned */
+  DPO_ERR_BETA = -4,         /* beta is not finite and > 0 */
+  DPO_ERR_LAYOUT = -5,       /* unknown pair layout / flag value */
+  DPO_ERR_WORKSPACE = -6,    /* workspace smaller than dpo_workspace_bytes() */
+  DPO_ERR_TARGET_RANGE = -7, /* device-detected target id outside [0, V) */
+  DPO_ERR_HIP = -8           /* a HIP runtime call failed */
+};
+
+/* Pair layouts of the concatenated batch.
+ * ADJACENT: rows 2i (chosen) and 2i+1 (rejected) - the Megatron-Bridge DPO
+ *   change ("feat(training): add DPO training with offline-scored reference
+ *   model", changelog) keeps a pair's rows next to each other.
+ * HALVES: rows i (chosen) and B+i (rejected) - the torchtune recipe
+ *   ("Run Distributed Full-Model DPO with PyTorch FSDP", step 4) and the
+ *   hand-written loss on "DPO Training on GPU, in depth" split the batch in
+ *   halves. */
+enum { DPO_PAIRS_ADJACENT = 0, DPO_PAIRS_HALVES = 1 };
+
+/* Operations for dpo_workspace_bytes(). */
+enum {
+  DPO_OP_SEQ_LOGPS = 0,
+  DPO_OP_REF_SCORE = 1,
+  DPO_OP_HEAD_BACKWARD = 2,
+  DPO_OP_LOGITS_SEQ_LOGPS = 3,
+  DPO_OP_LOGITS_BACKWARD = 4
+};
+
+/* Bytes of device workspace `op` needs for these sizes (H is ignored by the
+ * logits operations).  Returns 0 if the sizes break the shape rules or `op`
+ * is unknown.  Pure host arithmetic; touches no device. */
+size_t dpo_workspace_bytes(int op, int rows, int T, int H, int V);
+
+/* Sequence scores of the policy: for each row r,
+ *   logp_sum[r] = sum over completion positions t of log softmax(W h_{r,t})[y_{r,t}]
+ * ("DPO Training on GPU, in depth": "What one DPO step computes" and the
+ * hand-written loss in "A training configuration that fits"; sums, not
+ * averages, as the torchtune recipe's concatenated forward returns).
+ *   hidden   [rows, T, H] bf16  final hidden states
+ *   w_vocab  [V, H] bf16        LM-head weight (row v = token v)
+ *   targets  [rows, T] int32, mask [rows, T] uint8  (aligned, see above)
+ *   logp_sum [rows] float       the row scores (fp32)
+ *   logp_sum64 [rows] double    the same sums in fp64 (nullable); feed these
+ *                               to dpo_loss for a loss accurate to 1e-4
+ *   lse      [rows, T] float    per-position log-sum-exp over V, kept for the
+ *                               backward; 0 at mask-0 positions (nullable)
+ *   n_tokens [rows] int32       completion positions per row (nullable)
+ * The [rows, T, V] logits are never formed: the contraction runs on MFMA
+ * tiles and each tile keeps only a per-position running max and sum of
+ * exponentials plus the target logit. */
+int dpo_seq_logps(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t* targets,
+                  const uint8_t* mask, int rows, int T, int H, int V, float* logp_sum,
+                  double* logp_sum64, float* lse, int32_t* n_tokens, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Offline reference scoring: per-row completion log-prob sums, no beta applied
+ * ("feat(training): add DPO training with offline-scored reference model",
+ * section "Why the reference is scored offline"; "DPO Training on GPU, in
+ * depth", section "Four ways to host the reference model", item 3).  Same
+ * inputs as dpo_seq_logps; output ref_sum [rows] float. */
+int dpo_ref_score(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t* targets,
+                  const uint8_t* mask, int rows, int T, int H, int V, float* ref_sum,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* The sigmoid DPO loss ("DPO Training on GPU, in depth", sections "What one
+ * DPO step computes" and "A worked example of the numbers"), in fp64:
+ *   reward_r = beta (policy_r - ref_r);  margin_i = reward_chosen - reward_rejected
+ *   loss = mean over the num_pairs pairs of -log sigmoid(margin_i)
+ *   weight_r = -d loss / d policy_r = +beta sigmoid(-margin_i) / num_pairs on the
+ *              chosen row, the negative on the rejected row (the page's
+ *              per-pair gradient scale sigmoid(-margin))
+ *   accuracy = fraction of pairs with margin_i > 0 (strict)
+ *   policy_sum64 [2B] double, ref_sum [2B] float, layout DPO_PAIRS_*
+ *   loss [1] float; weight [2B] float; reward [2B], margin [B], accuracy [1]
+ *   float, each nullable.
+ * A caller that accumulates gradients over k micro-batches scales `weight`
+ * by 1/k before dpo_head_backward. */
+int dpo_loss(const double* policy_sum64, const float* ref_sum, int num_pairs, double beta,
+             int layout, float* loss, float* weight, float* reward, float* margin,
+             float* accuracy, void* stream);
+
+/* Head gradients of the loss through the row scores:
+ *   D_{r,t} = weight_r (softmax(W h_{r,t}) - onehot(y_{r,t}))   at completion positions
+ *   d_hidden[r,t,:] = D_{r,t} W      (exactly 0 at mask-0 positions)
+ *   d_w_vocab       = sum_{r,t} D_{r,t}^T h_{r,t}   (overwrite if accumulate_dw == 0,
+ *                                                    add to the existing values if 1)
+ * lse is the array dpo_seq_logps wrote; weight the array dpo_loss wrote.
+ * The logits are recomputed tile by tile (the page's chunked loss recomputes
+ * its log-softmax in backward the same way); D exists only as a bf16 operand
+ * in the workspace.  d_hidden [rows, T, H] and d_w_vocab [V, H] are fp32. */
+int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t* targets,
+                      const uint8_t* mask, int rows, int T, int H, int V, const float* lse,
+                      const float* weight, float* d_hidden, float* d_w_vocab, int accumulate_dw,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bandwidth-bound variant over pre-materialised logits [rows, T, V] bf16:
+ * the same scores as dpo_seq_logps, reading only completion positions. */
+int dpo_logits_seq_logps(const dpo_bf16* logits, const int32_t* targets, const uint8_t* mask,
+                         int rows, int T, int V, float* logp_sum, double* logp_sum64, float* lse,
+                         int32_t* n_tokens, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* dlogits [rows, T, V] bf16 (round to nearest even) = weight_r (softmax - onehot)
+ * at completion positions and exactly 0 elsewhere. */
+int dpo_logits_backward(const dpo_bf16* logits, const int32_t* targets, const uint8_t* mask,
+                        int rows, int T, int V, const float* lse, const float* weight,
+                        dpo_bf16* d_logits, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Waits for `stream`, then returns DPO_ERR_TARGET_RANGE if the most recent
+ * call that used `workspace` met a target id outside [0, V) at a completion
+ * position, DPO_OK otherwise (or DPO_ERR_HIP). */
+int dpo_device_status(void* workspace, void* stream);
+
+/* Static description of a status code. */
+const char* dpo_strerror(int status);
+
+/* Kernel timing.  While enabled, every kernel the library enqueues is
+ * bracketed by a pair of HIP events on its stream.  dpo_profile_count()
+ * waits for the recorded events and returns the number of distinct kernels
+ * seen; dpo_profile_entry() returns, for entry i, the kernel name, the summed
+ * duration in milliseconds and the number of launches.  Enabling (on=1) or
+ * disabling (on=0) clears what was collected. */
+int dpo_profile_enable(int on);
+int dpo_profile_count(void);
+int dpo_profile_entry(int i, const char** name, double* total_ms, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DPO_HEAD_H */

@@ -1,0 +1,506 @@
+// Host side of the C ABI declared in include/dpo_head.h: argument validation,
+// workspace layout, kernel sequencing on the caller's stream, device status
+// and optional per-kernel timing.  No device memory is allocated here.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/dpo_head.h"
+#include "dpo_common.h"
+#include "gemm_core.h"
+#include "launch.h"
+
+using namespace dpo;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// workspace layout
+// ---------------------------------------------------------------------------
+struct Layout {
+  int Mp = 0;   // completion positions rounded up to the GEMM tile (upper bound rows*T)
+  int Vp = 0;   // vocabulary rounded up to the GEMM tile
+  int nVt = 0;  // vocabulary tiles of the forward contraction
+  size_t hdr = 0, idx = 0, tgt = 0, rowc = 0, rowoff = 0;
+  size_t part = 0, tlogit = 0, lse64 = 0, logp64 = 0;
+  size_t D = 0, DT = 0, WT = 0, HT = 0;
+  size_t total = 0;
+};
+
+bool shape_ok(int rows, int T, int H, int V, bool need_h) {
+  if (rows <= 0 || (rows & 1) || T <= 0 || V <= 0 || (V % 8)) return false;
+  if ((long long)rows * T >= (1LL << 31) - gemm::BM) return false;
+  if (V >= (1 << 30)) return false;
+  if (need_h && (H <= 0 || H % 64 || H >= (1 << 30))) return false;
+  return true;
+}
+
+Layout make_layout(int op, int rows, int T, int H, int V) {
+  Layout L;
+  const size_t A = 256;
+  const long long positions = (long long)rows * T;
+  L.Mp = (int)align_up((size_t)positions, gemm::BM);
+  L.Vp = (int)align_up((size_t)V, gemm::BN);
+  L.nVt = cdiv(V, gemm::BN);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, A);
+    return at;
+  };
+  L.hdr = take(sizeof(WsHeader));
+  if (op == DPO_OP_LOGITS_BACKWARD) {
+    L.total = o;
+    return L;
+  }
+  L.idx = take((size_t)L.Mp * 4);
+  L.tgt = take((size_t)L.Mp * 4);
+  L.rowc = take((size_t)L.Mp * 4);
+  L.rowoff = take((size_t)(rows + 1) * 4);
+  if (op == DPO_OP_SEQ_LOGPS || op == DPO_OP_REF_SCORE) {
+    L.part = take((size_t)L.nVt * L.Mp * sizeof(float2));
+    L.tlogit = take((size_t)L.Mp * 4);
+  }
+  if (op != DPO_OP_HEAD_BACKWARD) {
+    L.lse64 = take((size_t)L.Mp * 8);
+    L.logp64 = take((size_t)L.Mp * 8);
+  }
+  if (op == DPO_OP_HEAD_BACKWARD) {
+    L.D = take((size_t)L.Mp * L.Vp * 2);
+    L.DT = take((size_t)L.Vp * L.Mp * 2);
+    L.WT = take((size_t)H * L.Vp * 2);
+    L.HT = take((size_t)H * L.Mp * 2);
+  }
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// device facts
+// ---------------------------------------------------------------------------
+int persistent_grid() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Tile-group widths (m-tiles per group) of the persistent scheduler.
+constexpr int kGroupFwd = 8;
+constexpr int kGroupBwd = 4;
+
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+struct ProfSum {
+  std::string name;
+  double ms;
+  int n;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_pending;
+std::vector<ProfSum> g_prof_sums;
+
+void prof_clear_locked() {
+  for (auto& r : g_prof_pending) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_prof_pending.clear();
+  g_prof_sums.clear();
+}
+
+void prof_drain_locked() {
+  for (auto& r : g_prof_pending) {
+    float ms = 0.f;
+    hipEventSynchronize(r.b);
+    hipEventElapsedTime(&ms, r.a, r.b);
+    bool found = false;
+    for (auto& s : g_prof_sums)
+      if (s.name == r.name) {
+        s.ms += ms;
+        s.n += 1;
+        found = true;
+        break;
+      }
+    if (!found) g_prof_sums.push_back({r.name, (double)ms, 1});
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_prof_pending.clear();
+}
+
+// Runs `f` (which enqueues one kernel on `s`), bracketed by events when timing is on.
+template <typename F>
+hipError_t timed(const char* name, hipStream_t s, F f) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    on = g_prof_on;
+  }
+  if (!on) return f();
+  hipEvent_t a, b;
+  if (hipEventCreate(&a) != hipSuccess) return hipErrorUnknown;
+  if (hipEventCreate(&b) != hipSuccess) {
+    hipEventDestroy(a);
+    return hipErrorUnknown;
+  }
+  hipEventRecord(a, s);
+  hipError_t e = f();
+  hipEventRecord(b, s);
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_prof_pending.push_back({name, a, b});
+  return e;
+}
+
+#define RUN(name, call)                                     \
+  do {                                                      \
+    hipError_t _e = timed(name, st, [&]() { return call; }); \
+    if (_e != hipSuccess) return DPO_ERR_HIP;               \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// shared pieces of the entry points
+// ---------------------------------------------------------------------------
+int check_common(const void* targets, const void* mask, int rows, int T, int H, int V, bool need_h,
+                 int op, size_t ws_bytes, const void* ws) {
+  if (!targets || !mask || !ws) return DPO_ERR_NULL;
+  if (!shape_ok(rows, T, H, V, need_h)) return DPO_ERR_SHAPE;
+  if (!aligned16(ws)) return DPO_ERR_ALIGN;
+  if (ws_bytes < make_layout(op, rows, T, H, V).total) return DPO_ERR_WORKSPACE;
+  return DPO_OK;
+}
+
+int enqueue_compact(const Layout& L, void* ws, const int32_t* targets, const uint8_t* mask, int rows,
+                    int T, int V, float* lse_out, hipStream_t st) {
+  CompactArgs c;
+  c.mask = mask;
+  c.targets = targets;
+  c.rows = rows;
+  c.T = T;
+  c.V = V;
+  c.Mp = L.Mp;
+  c.hdr = at<WsHeader>(ws, L.hdr);
+  c.idx = at<int>(ws, L.idx);
+  c.tgt_c = at<int>(ws, L.tgt);
+  c.row_c = at<int>(ws, L.rowc);
+  c.row_off = at<int>(ws, L.rowoff);
+  c.lse_out = lse_out;
+  RUN("compact", launch_compact(c, st));
+  return DPO_OK;
+}
+
+int enqueue_fused_forward(const dpo_bf16* hidden, const dpo_bf16* w, const int32_t* targets,
+                          const uint8_t* mask, int rows, int T, int H, int V, float* sum32,
+                          double* sum64, float* lse, int32_t* n_tokens, void* ws, int op,
+                          hipStream_t st) {
+  const Layout L = make_layout(op, rows, T, H, V);
+  int rc = enqueue_compact(L, ws, targets, mask, rows, T, V, lse, st);
+  if (rc) return rc;
+  FwdArgs f;
+  f.hidden = hidden;
+  f.w = w;
+  f.H = H;
+  f.V = V;
+  f.Mp = L.Mp;
+  f.gm = kGroupFwd;
+  f.idx = at<int>(ws, L.idx);
+  f.tgt_c = at<int>(ws, L.tgt);
+  f.hdr = at<WsHeader>(ws, L.hdr);
+  f.part = at<float2>(ws, L.part);
+  f.tgt_logit = at<float>(ws, L.tlogit);
+  RUN("fwd_gemm", launch_fwd_gemm(f, persistent_grid(), st));
+  CombineArgs c;
+  c.part = f.part;
+  c.tgt_logit = f.tgt_logit;
+  c.tgt_c = f.tgt_c;
+  c.idx = f.idx;
+  c.hdr = f.hdr;
+  c.Mp = L.Mp;
+  c.nVt = L.nVt;
+  c.lse64 = at<double>(ws, L.lse64);
+  c.logp64 = at<double>(ws, L.logp64);
+  c.lse_out = lse;
+  RUN("combine", launch_combine(c, st));
+  RowSumArgs r;
+  r.logp64 = c.logp64;
+  r.row_off = at<int>(ws, L.rowoff);
+  r.hdr = f.hdr;
+  r.rows = rows;
+  r.sum32 = sum32;
+  r.sum64 = sum64;
+  r.n_tokens = n_tokens;
+  RUN("row_sums", launch_row_sums(r, st));
+  return DPO_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+size_t dpo_workspace_bytes(int op, int rows, int T, int H, int V) {
+  if (op < DPO_OP_SEQ_LOGPS || op > DPO_OP_LOGITS_BACKWARD) return 0;
+  const bool need_h = op <= DPO_OP_HEAD_BACKWARD;
+  if (!shape_ok(rows, T, H, V, need_h)) return 0;
+  return make_layout(op, rows, T, need_h ? H : 0, V).total;
+}
+
+int dpo_seq_logps(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t* targets,
+                  const uint8_t* mask, int rows, int T, int H, int V, float* logp_sum,
+                  double* logp_sum64, float* lse, int32_t* n_tokens, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!hidden || !w_vocab || !logp_sum) return DPO_ERR_NULL;
+  int rc = check_common(targets, mask, rows, T, H, V, true, DPO_OP_SEQ_LOGPS, workspace_bytes, workspace);
+  if (rc) return rc;
+  if (!aligned16(hidden) || !aligned16(w_vocab) || !aligned16(logp_sum) ||
+      (logp_sum64 && !aligned16(logp_sum64)) || (lse && !aligned16(lse)))
+    return DPO_ERR_ALIGN;
+  return enqueue_fused_forward(hidden, w_vocab, targets, mask, rows, T, H, V, logp_sum, logp_sum64,
+                               lse, n_tokens, workspace, DPO_OP_SEQ_LOGPS, (hipStream_t)stream);
+}
+
+int dpo_ref_score(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t* targets,
+                  const uint8_t* mask, int rows, int T, int H, int V, float* ref_sum,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!hidden || !w_vocab || !ref_sum) return DPO_ERR_NULL;
+  int rc = check_common(targets, mask, rows, T, H, V, true, DPO_OP_REF_SCORE, workspace_bytes, workspace);
+  if (rc) return rc;
+  if (!aligned16(hidden) || !aligned16(w_vocab) || !aligned16(ref_sum)) return DPO_ERR_ALIGN;
+  return enqueue_fused_forward(hidden, w_vocab, targets, mask, rows, T, H, V, ref_sum, nullptr,
+                               nullptr, nullptr, workspace, DPO_OP_REF_SCORE, (hipStream_t)stream);
+}
+
+int dpo_loss(const double* policy_sum64, const float* ref_sum, int num_pairs, double beta, int layout,
+             float* loss, float* weight, float* reward, float* margin, float* accuracy, void* stream) {
+  if (!policy_sum64 || !ref_sum || !loss || !weight) return DPO_ERR_NULL;
+  if (num_pairs <= 0 || num_pairs >= (1 << 29)) return DPO_ERR_SHAPE;
+  if (!(isfinite(beta) && beta > 0.0)) return DPO_ERR_BETA;
+  if (layout != DPO_PAIRS_ADJACENT && layout != DPO_PAIRS_HALVES) return DPO_ERR_LAYOUT;
+  hipStream_t st = (hipStream_t)stream;
+  LossArgs a;
+  a.policy = policy_sum64;
+  a.ref = ref_sum;
+  a.num_pairs = num_pairs;
+  a.layout = layout;
+  a.beta = beta;
+  a.loss = loss;
+  a.weight = weight;
+  a.reward = reward;
+  a.margin = margin;
+  a.accuracy = accuracy;
+  RUN("loss", launch_loss(a, st));
+  return DPO_OK;
+}
+
+int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t* targets,
+                      const uint8_t* mask, int rows, int T, int H, int V, const float* lse,
+                      const float* weight, float* d_hidden, float* d_w_vocab, int accumulate_dw,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!hidden || !w_vocab || !lse || !weight || !d_hidden || !d_w_vocab) return DPO_ERR_NULL;
+  int rc = check_common(targets, mask, rows, T, H, V, true, DPO_OP_HEAD_BACKWARD, workspace_bytes,
+                        workspace);
+  if (rc) return rc;
+  if (accumulate_dw != 0 && accumulate_dw != 1) return DPO_ERR_LAYOUT;
+  if (!aligned16(hidden) || !aligned16(w_vocab) || !aligned16(lse) || !aligned16(d_hidden) ||
+      !aligned16(d_w_vocab))
+    return DPO_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const Layout L = make_layout(DPO_OP_HEAD_BACKWARD, rows, T, H, V);
+  void* ws = workspace;
+  rc = enqueue_compact(L, ws, targets, mask, rows, T, V, nullptr, st);
+  if (rc) return rc;
+  WsHeader* hdr = at<WsHeader>(ws, L.hdr);
+  uint16_t* D = at<uint16_t>(ws, L.D);
+  uint16_t* DT = at<uint16_t>(ws, L.DT);
+  uint16_t* WT = at<uint16_t>(ws, L.WT);
+  uint16_t* HT = at<uint16_t>(ws, L.HT);
+
+  TransposeWArgs tw{w_vocab, V, H, L.Vp, WT};
+  RUN("transpose_w", launch_transpose_w(tw, st));
+  GatherHTArgs gh{hidden, at<int>(ws, L.idx), hdr, H, L.Mp, HT};
+  RUN("gather_ht", launch_gather_ht(gh, st));
+
+  DProdArgs dp;
+  dp.hidden = hidden;
+  dp.w = w_vocab;
+  dp.H = H;
+  dp.V = V;
+  dp.Vp = L.Vp;
+  dp.Mp = L.Mp;
+  dp.gm = kGroupFwd;
+  dp.idx = at<int>(ws, L.idx);
+  dp.tgt_c = at<int>(ws, L.tgt);
+  dp.row_c = at<int>(ws, L.rowc);
+  dp.hdr = hdr;
+  dp.lse = lse;
+  dp.weight = weight;
+  dp.D = D;
+  dp.DT = DT;
+  RUN("dlogits_gemm", launch_dprod_gemm(dp, persistent_grid(), st));
+
+  DhArgs dh;
+  dh.D = D;
+  dh.wt = WT;
+  dh.H = H;
+  dh.Vp = L.Vp;
+  dh.Mp = L.Mp;
+  dh.gm = kGroupBwd;
+  dh.idx = dp.idx;
+  dh.hdr = hdr;
+  dh.d_hidden = d_hidden;
+  RUN("dhidden_gemm", launch_dh_gemm(dh, persistent_grid(), st));
+
+  ZeroRowsArgs z{mask, H, d_hidden};
+  RUN("zero_rows", launch_zero_rows(z, (long)rows * T, st));
+
+  DwArgs dw;
+  dw.DT = DT;
+  dw.ht = HT;
+  dw.V = V;
+  dw.H = H;
+  dw.Vp = L.Vp;
+  dw.Mp = L.Mp;
+  dw.gm = kGroupBwd;
+  dw.accumulate = accumulate_dw;
+  dw.hdr = hdr;
+  dw.d_w = d_w_vocab;
+  RUN("dw_gemm", launch_dw_gemm(dw, persistent_grid(), st));
+  return DPO_OK;
+}
+
+int dpo_logits_seq_logps(const dpo_bf16* logits, const int32_t* targets, const uint8_t* mask, int rows,
+                         int T, int V, float* logp_sum, double* logp_sum64, float* lse,
+                         int32_t* n_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !logp_sum) return DPO_ERR_NULL;
+  int rc = check_common(targets, mask, rows, T, 0, V, false, DPO_OP_LOGITS_SEQ_LOGPS, workspace_bytes,
+                        workspace);
+  if (rc) return rc;
+  if (!aligned16(logits) || !aligned16(logp_sum) || (logp_sum64 && !aligned16(logp_sum64)) ||
+      (lse && !aligned16(lse)))
+    return DPO_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const Layout L = make_layout(DPO_OP_LOGITS_SEQ_LOGPS, rows, T, 0, V);
+  void* ws = workspace;
+  rc = enqueue_compact(L, ws, targets, mask, rows, T, V, lse, st);
+  if (rc) return rc;
+  StreamFwdArgs f;
+  f.logits = logits;
+  f.V = V;
+  f.idx = at<int>(ws, L.idx);
+  f.tgt_c = at<int>(ws, L.tgt);
+  f.hdr = at<WsHeader>(ws, L.hdr);
+  f.lse64 = at<double>(ws, L.lse64);
+  f.logp64 = at<double>(ws, L.logp64);
+  f.lse_out = lse;
+  RUN("stream_fwd", launch_stream_fwd(f, (long)rows * T, st));
+  RowSumArgs r;
+  r.logp64 = f.logp64;
+  r.row_off = at<int>(ws, L.rowoff);
+  r.hdr = f.hdr;
+  r.rows = rows;
+  r.sum32 = logp_sum;
+  r.sum64 = logp_sum64;
+  r.n_tokens = n_tokens;
+  RUN("row_sums", launch_row_sums(r, st));
+  return DPO_OK;
+}
+
+int dpo_logits_backward(const dpo_bf16* logits, const int32_t* targets, const uint8_t* mask, int rows,
+                        int T, int V, const float* lse, const float* weight, dpo_bf16* d_logits,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !lse || !weight || !d_logits) return DPO_ERR_NULL;
+  int rc = check_common(targets, mask, rows, T, 0, V, false, DPO_OP_LOGITS_BACKWARD, workspace_bytes,
+                        workspace);
+  if (rc) return rc;
+  if (!aligned16(logits) || !aligned16(lse) || !aligned16(d_logits)) return DPO_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const Layout L = make_layout(DPO_OP_LOGITS_BACKWARD, rows, T, 0, V);
+  WsHeader* hdr = at<WsHeader>(workspace, L.hdr);
+  RUN("reset_status", launch_reset_status(hdr, st));
+  StreamBwdArgs b;
+  b.logits = logits;
+  b.targets = targets;
+  b.mask = mask;
+  b.T = T;
+  b.V = V;
+  b.lse = lse;
+  b.weight = weight;
+  b.hdr = hdr;
+  b.d_logits = d_logits;
+  RUN("stream_bwd", launch_stream_bwd(b, (long)rows * T, st));
+  return DPO_OK;
+}
+
+int dpo_device_status(void* workspace, void* stream) {
+  if (!workspace) return DPO_ERR_NULL;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DPO_ERR_HIP;
+  int status = 0;
+  if (hipMemcpy(&status, workspace, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return DPO_ERR_HIP;
+  return (status & kStatusTargetRange) ? DPO_ERR_TARGET_RANGE : DPO_OK;
+}
+
+const char* dpo_strerror(int status) {
+  switch (status) {
+    case DPO_OK: return "ok";
+    case DPO_ERR_NULL: return "a required pointer is NULL";
+    case DPO_ERR_SHAPE: return "sizes break the shape rules (rows even > 0, T,H,V > 0, H % 64 == 0, V % 8 == 0)";
+    case DPO_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case DPO_ERR_BETA: return "beta must be finite and > 0";
+    case DPO_ERR_LAYOUT: return "unknown pair layout or flag value";
+    case DPO_ERR_WORKSPACE: return "workspace smaller than dpo_workspace_bytes()";
+    case DPO_ERR_TARGET_RANGE: return "a target id at a completion position is outside [0, V)";
+    case DPO_ERR_HIP: return "a HIP runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+int dpo_profile_enable(int on) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  prof_drain_locked();
+  prof_clear_locked();
+  g_prof_on = on != 0;
+  return DPO_OK;
+}
+
+int dpo_profile_count(void) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  prof_drain_locked();
+  return (int)g_prof_sums.size();
+}
+
+int dpo_profile_entry(int i, const char** name, double* total_ms, int* launches) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  prof_drain_locked();
+  if (i < 0 || i >= (int)g_prof_sums.size()) return DPO_ERR_SHAPE;
+  if (name) *name = g_prof_sums[i].name.c_str();
+  if (total_ms) *total_ms = g_prof_sums[i].ms;
+  if (launches) *launches = g_prof_sums[i].n;
+  return DPO_OK;
+}
+
+}  // extern "C"

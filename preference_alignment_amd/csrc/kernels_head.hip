@@ -1,0 +1,483 @@
+// Fused LM-head kernels of the DPO sequence log-probability path (gfx950).
+//
+// The method ("DPO Training on GPU, in depth", sections "What one DPO step
+// computes" and "A training configuration that fits"): for every completion
+// position t of row r, z_t = W_vocab . h_t over the whole vocabulary,
+// log p_t = z_t[y_t] - logsumexp(z_t), and the row score is the sum of log p_t
+// over the completion positions of the row.  The backward of the sigmoid DPO
+// loss through that score is dz_t = w_r (softmax(z_t) - onehot(y_t)), giving
+// dHidden_t = dz_t . W_vocab and dW_vocab = sum_t dz_t^T h_t.  The page's
+// hand-written loss recomputes the fp32 log-softmax in backward instead of
+// keeping it; the fused path here does the same with the contraction itself,
+// so no [rows x T x V] logits tensor ever exists.
+//
+// Kernels, in call order:
+//   k_compact        completion positions (row-major), per-row offsets, targets check
+//   k_fwd_gemm       Z tile = Hc . W^T on MFMA; epilogue: per-row (max, sum exp) over
+//                    the tile's columns and capture of the target logit
+//   k_combine        fp64 combine of the per-tile (max, sum exp) -> lse, log p
+//   k_row_sums       fp64 per-row sums in a fixed order
+//   k_transpose_w    W^T (bf16) for the dHidden contraction
+//   k_gather_ht      Hc^T (bf16) for the dW contraction
+//   k_dprod_gemm     recompute Z tile; epilogue D = w (exp(z - lse) - onehot) -> bf16 D, D^T
+//   k_dh_gemm        dHidden rows = D . W, scattered to their positions
+//   k_dw_gemm        dW_vocab = D^T . Hc (overwrite or accumulate)
+//   k_zero_rows      dHidden = 0 at positions outside the completion mask
+#include "dpo_common.h"
+#include "gemm_core.h"
+#include "launch.h"
+
+namespace dpo {
+using namespace gemm;
+
+// ---------------------------------------------------------------------------
+// completion positions
+// ---------------------------------------------------------------------------
+constexpr int kCompactThreads = 1024;
+
+__global__ __launch_bounds__(kCompactThreads) void k_compact(CompactArgs a) {
+  __shared__ int scan[kCompactThreads];
+  __shared__ int err;
+  const int tid = threadIdx.x;
+  const long N = (long)a.rows * a.T;
+  const long per = (N + kCompactThreads - 1) / kCompactThreads;
+  const long lo = min(N, per * tid);
+  const long hi = min(N, lo + per);
+  if (tid == 0) err = 0;
+  int cnt = 0;
+  for (long p = lo; p < hi; ++p) cnt += a.mask[p] != 0;
+  scan[tid] = cnt;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the thread counts
+  for (int o = 1; o < kCompactThreads; o <<= 1) {
+    int v = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  int pos = scan[tid] - cnt;
+  const int n_c = scan[kCompactThreads - 1];
+  int bad = 0;
+  for (long p = lo; p < hi; ++p) {
+    if (p % a.T == 0) a.row_off[p / a.T] = pos;
+    if (a.mask[p] != 0) {
+      int t = a.targets[p];
+      if (t < 0 || t >= a.V) {
+        bad = 1;
+        t = -1;
+      }
+      a.idx[pos] = (int)p;
+      a.tgt_c[pos] = t;
+      a.row_c[pos] = (int)(p / a.T);
+      ++pos;
+    } else if (a.lse_out) {
+      a.lse_out[p] = 0.f;
+    }
+  }
+  if (bad) atomicOr(&err, kStatusTargetRange);
+  // padding entries up to the padded position count: a valid row, no target
+  for (long m = n_c + tid; m < a.Mp; m += kCompactThreads) {
+    a.idx[m] = 0;
+    a.tgt_c[m] = -1;
+    a.row_c[m] = 0;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    a.row_off[a.rows] = n_c;
+    a.hdr->n_c = n_c;
+    a.hdr->status = err;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// forward contraction with the online log-sum-exp epilogue
+// ---------------------------------------------------------------------------
+constexpr int kEpiBytes = 8192;  // per-row staging + cross-wave reduction
+
+__global__ __launch_bounds__(NTHREADS, 1) void k_fwd_gemm(FwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int* tgt_s = (int*)(smem + PIPE_BYTES);                  // 256 ints
+  float2* red = (float2*)(smem + PIPE_BYTES + 1024);       // [2][256]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n_c = a.hdr->n_c;
+  Sched sc;
+  sc.init(cdiv(n_c, BM), cdiv(a.V, BN), a.gm);
+  const int lchunk = loader_lchunk(tid);
+  for (int t = sc.begin; t < sc.end; t += sc.step) {
+    int mt, nt;
+    sc.coords(t, mt, nt);
+    const int m0 = mt * BM, n0 = nt * BN;
+    const uint16_t* arows[LOADS_PER_THREAD];
+    const uint16_t* brows[LOADS_PER_THREAD];
+#pragma unroll
+    for (int it = 0; it < LOADS_PER_THREAD; ++it) {
+      const int r = loader_row(it, tid);
+      arows[it] = a.hidden + (size_t)a.idx[m0 + r] * a.H + lchunk * 8;
+      brows[it] = a.w + (size_t)min(n0 + r, a.V - 1) * a.H + lchunk * 8;
+    }
+    tgt_s[tid] = a.tgt_c[m0 + tid];
+    Acc acc;
+    mainloop(acc, arows, brows, a.H / BK, smem, wave, lane, wm, wn);
+
+    const int cbase = n0 + wn * 128;  // first column of this wave
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = acc_row(wm, i, e, lane);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (cbase + j * 32 + (lane & 31) < a.V) mx = fmaxf(mx, acc.c[i][j][e]);
+        mx = half_max(mx);
+        float s = 0.f;
+        const float mxl = mx * kLog2e;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (cbase + j * 32 + (lane & 31) < a.V) s += fast_exp2(fmaf(acc.c[i][j][e], kLog2e, -mxl));
+        s = half_sum(s);
+        const int off = tgt_s[row] - cbase;
+        if (off >= 0 && off < 128 && (off & 31) == (lane & 31) && m0 + row < n_c) {
+          const int jj = off >> 5;
+          float v = acc.c[i][0][e];
+          v = jj == 1 ? acc.c[i][1][e] : v;
+          v = jj == 2 ? acc.c[i][2][e] : v;
+          v = jj == 3 ? acc.c[i][3][e] : v;
+          a.tgt_logit[m0 + row] = v;
+        }
+        if ((lane & 31) == 0) red[wn * 256 + row] = make_float2(mx, s);
+      }
+    }
+    __syncthreads();
+    {
+      const float2 p0 = red[tid], p1 = red[256 + tid];
+      const float M = fmaxf(p0.x, p1.x);
+      const float S = p0.y * fast_exp2((p0.x - M) * kLog2e) + p1.y * fast_exp2((p1.x - M) * kLog2e);
+      if (m0 + tid < n_c) a.part[(size_t)nt * a.Mp + m0 + tid] = make_float2(M, S);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine per-tile partials: lse = M + log(sum_j s_j exp(m_j - M)), in fp64
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  const int n_c = a.hdr->n_c;
+  if (m >= n_c) return;
+  float M = -INFINITY;
+  for (int j = 0; j < a.nVt; ++j) M = fmaxf(M, a.part[(size_t)j * a.Mp + m].x);
+  double S = 0.0;
+  for (int j = 0; j < a.nVt; ++j) {
+    const float2 p = a.part[(size_t)j * a.Mp + m];
+    S += (double)p.y * exp((double)p.x - (double)M);
+  }
+  const double lse = (double)M + log(S);
+  const int t = a.tgt_c[m];
+  a.lse64[m] = lse;
+  a.logp64[m] = t >= 0 ? (double)a.tgt_logit[m] - lse : __builtin_nan("");
+  if (a.lse_out) a.lse_out[a.idx[m]] = (float)lse;
+}
+
+// ---------------------------------------------------------------------------
+// per-row sums of log p in fp64, fixed reduction order
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_row_sums(RowSumArgs a) {
+  __shared__ double red[256];
+  const int r = blockIdx.x;
+  const int lo = a.row_off[r];
+  const int hi = r + 1 < a.rows ? a.row_off[r + 1] : a.hdr->n_c;
+  double s = 0.0;
+  for (int m = lo + threadIdx.x; m < hi; m += 256) s += a.logp64[m];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double v = red[0];
+    if (a.sum32) a.sum32[r] = (float)v;
+    if (a.sum64) a.sum64[r] = v;
+    if (a.n_tokens) a.n_tokens[r] = hi - lo;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// operand transposes for the backward contractions
+// ---------------------------------------------------------------------------
+// W [V, H] -> WT [H, Vp], zero columns v >= V.  64x64 tiles through LDS.
+__global__ __launch_bounds__(256) void k_transpose_w(TransposeWArgs a) {
+  __shared__ uint16_t tile[64][66];
+  const int v0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int v = v0 + r;
+    tile[r][tx] = v < a.V ? a.w[(size_t)v * a.H + h0 + tx] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) a.wt[(size_t)(h0 + r) * a.Vp + v0 + tx] = tile[tx][r];
+}
+
+// hidden rows at completion positions -> HT [H, Mp], zero columns m >= n_c.
+__global__ __launch_bounds__(256) void k_gather_ht(GatherHTArgs a) {
+  __shared__ uint16_t tile[64][66];
+  const int n_c = a.hdr->n_c;
+  const int m0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
+  if (m0 >= (int)align_up((size_t)n_c, BM)) return;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int m = m0 + r;
+    tile[r][tx] = m < n_c ? a.hidden[(size_t)a.idx[m] * a.H + h0 + tx] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) a.ht[(size_t)(h0 + r) * a.Mp + m0 + tx] = tile[tx][r];
+}
+
+// ---------------------------------------------------------------------------
+// backward: recompute Z, D = w (exp(z - lse) - onehot) in bf16, both layouts
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NTHREADS, 1) void k_dprod_gemm(DProdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int* tgt_s = (int*)(smem + PIPE_BYTES);
+  float* lse_s = (float*)(smem + PIPE_BYTES + 1024);
+  float* w_s = (float*)(smem + PIPE_BYTES + 2048);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n_c = a.hdr->n_c;
+  Sched sc;
+  sc.init(cdiv(n_c, BM), a.Vp / BN, a.gm);
+  const int lchunk = loader_lchunk(tid);
+  for (int t = sc.begin; t < sc.end; t += sc.step) {
+    int mt, nt;
+    sc.coords(t, mt, nt);
+    const int m0 = mt * BM, n0 = nt * BN;
+    const uint16_t* arows[LOADS_PER_THREAD];
+    const uint16_t* brows[LOADS_PER_THREAD];
+#pragma unroll
+    for (int it = 0; it < LOADS_PER_THREAD; ++it) {
+      const int r = loader_row(it, tid);
+      arows[it] = a.hidden + (size_t)a.idx[m0 + r] * a.H + lchunk * 8;
+      brows[it] = a.w + (size_t)min(n0 + r, a.V - 1) * a.H + lchunk * 8;
+    }
+    {
+      const int m = m0 + tid;
+      const bool live = m < n_c;
+      tgt_s[tid] = live ? a.tgt_c[m] : -1;
+      lse_s[tid] = live ? a.lse[a.idx[m]] * kLog2e : 0.f;
+      w_s[tid] = live ? a.weight[a.row_c[m]] : 0.f;
+    }
+    Acc acc;
+    mainloop(acc, arows, brows, a.H / BK, smem, wave, lane, wm, wn);
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float d[FN][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int e = q * 4 + s;
+          const int row = acc_row(wm, i, e, lane);
+          const int tg = tgt_s[row];
+          const float L = lse_s[row];
+          const float wr = w_s[row];
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int col = n0 + acc_col(wn, j, lane);
+            const float p = fast_exp2(fmaf(acc.c[i][j][e], kLog2e, -L));
+            float dv = wr * (p - (col == tg ? 1.f : 0.f));
+            dv = col < a.V ? dv : 0.f;
+            d[j][s] = dv;
+            const int m = m0 + row;
+            a.D[(size_t)m * a.Vp + col] = (uint16_t)(pack_bf16x2(dv, 0.f) & 0xffffu);
+          }
+        }
+        const int mrow = m0 + acc_row(wm, i, q * 4, lane);  // first of 4 consecutive rows
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = n0 + acc_col(wn, j, lane);
+          uint2 pk;
+          pk.x = pack_bf16x2(d[j][0], d[j][1]);
+          pk.y = pack_bf16x2(d[j][2], d[j][3]);
+          *(uint2*)(a.DT + (size_t)col * a.Mp + mrow) = pk;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dHidden = D . W  (A = D rows, B = W^T rows), scattered to positions
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NTHREADS, 1) void k_dh_gemm(DhArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n_c = a.hdr->n_c;
+  Sched sc;
+  sc.init(cdiv(n_c, BM), cdiv(a.H, BN), a.gm);
+  const int lchunk = loader_lchunk(tid);
+  for (int t = sc.begin; t < sc.end; t += sc.step) {
+    int mt, nt;
+    sc.coords(t, mt, nt);
+    const int m0 = mt * BM, n0 = nt * BN;
+    const uint16_t* arows[LOADS_PER_THREAD];
+    const uint16_t* brows[LOADS_PER_THREAD];
+#pragma unroll
+    for (int it = 0; it < LOADS_PER_THREAD; ++it) {
+      const int r = loader_row(it, tid);
+      arows[it] = a.D + (size_t)(m0 + r) * a.Vp + lchunk * 8;
+      brows[it] = a.wt + (size_t)min(n0 + r, a.H - 1) * a.Vp + lchunk * 8;
+    }
+    Acc acc;
+    mainloop(acc, arows, brows, a.Vp / BK, smem, wave, lane, wm, wn);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + acc_row(wm, i, e, lane);
+        if (m >= n_c) continue;
+        float* dst = a.d_hidden + (size_t)a.idx[m] * a.H;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = n0 + acc_col(wn, j, lane);
+          if (col < a.H) dst[col] = acc.c[i][j][e];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dW_vocab = D^T . Hc  (A = D^T rows, B = Hc^T rows), K = completion positions
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NTHREADS, 1) void k_dw_gemm(DwArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n_c = a.hdr->n_c;
+  const int nk = cdiv(n_c, BK);
+  Sched sc;
+  sc.init(a.Vp / BM, cdiv(a.H, BN), a.gm);
+  const int lchunk = loader_lchunk(tid);
+  for (int t = sc.begin; t < sc.end; t += sc.step) {
+    int mt, nt;
+    sc.coords(t, mt, nt);
+    const int m0 = mt * BM, n0 = nt * BN;
+    const uint16_t* arows[LOADS_PER_THREAD];
+    const uint16_t* brows[LOADS_PER_THREAD];
+#pragma unroll
+    for (int it = 0; it < LOADS_PER_THREAD; ++it) {
+      const int r = loader_row(it, tid);
+      arows[it] = a.DT + (size_t)(m0 + r) * a.Mp + lchunk * 8;
+      brows[it] = a.ht + (size_t)min(n0 + r, a.H - 1) * a.Mp + lchunk * 8;
+    }
+    Acc acc;
+    mainloop(acc, arows, brows, nk, smem, wave, lane, wm, wn);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int v = m0 + acc_row(wm, i, e, lane);
+        if (v >= a.V) continue;
+        float* dst = a.d_w + (size_t)v * a.H;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = n0 + acc_col(wn, j, lane);
+          if (col < a.H) dst[col] = a.accumulate ? dst[col] + acc.c[i][j][e] : acc.c[i][j][e];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// dHidden rows outside the completion mask are exactly zero.
+__global__ __launch_bounds__(256) void k_zero_rows(ZeroRowsArgs a) {
+  const long p = blockIdx.x;
+  if (a.mask[p] != 0) return;
+  float4* dst = (float4*)(a.d_hidden + p * a.H);
+  for (int c = threadIdx.x; c < a.H / 4; c += 256) dst[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+static int gemm_lds_bytes() { return PIPE_BYTES + kEpiBytes; }
+
+static hipError_t prep_gemm(const void* fn) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes());
+}
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_gemm(const FwdArgs& a, int grid, hipStream_t s) {
+  static hipError_t once = prep_gemm((const void*)k_fwd_gemm);
+  if (once != hipSuccess) return once;
+  hipLaunchKernelGGL(k_fwd_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_combine, dim3(a.Mp / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_sums(const RowSumArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_row_sums, dim3(a.rows), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_w(const TransposeWArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_transpose_w, dim3(a.Vp / 64, a.H / 64), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_ht(const GatherHTArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_gather_ht, dim3(a.Mp / 64, a.H / 64), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dprod_gemm(const DProdArgs& a, int grid, hipStream_t s) {
+  static hipError_t once = prep_gemm((const void*)k_dprod_gemm);
+  if (once != hipSuccess) return once;
+  hipLaunchKernelGGL(k_dprod_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dh_gemm(const DhArgs& a, int grid, hipStream_t s) {
+  static hipError_t once = prep_gemm((const void*)k_dh_gemm);
+  if (once != hipSuccess) return once;
+  hipLaunchKernelGGL(k_dh_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw_gemm(const DwArgs& a, int grid, hipStream_t s) {
+  static hipError_t once = prep_gemm((const void*)k_dw_gemm);
+  if (once != hipSuccess) return once;
+  hipLaunchKernelGGL(k_dw_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_rows(const ZeroRowsArgs& a, long positions, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_rows, dim3((unsigned)positions), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dpo

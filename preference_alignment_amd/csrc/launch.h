@@ -1,0 +1,158 @@
+// Internal interface between the C-ABI host code and the kernel files.
+// Argument structs are passed by value to kernels; all pointers are device
+// pointers.  Nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dpo_common.h"
+
+namespace dpo {
+
+struct CompactArgs {
+  const uint8_t* mask;
+  const int32_t* targets;
+  int rows, T, V, Mp;
+  WsHeader* hdr;
+  int* idx;      // [Mp] flat position r*T+t of each completion position
+  int* tgt_c;    // [Mp] its target (-1: padding or out of range)
+  int* row_c;    // [Mp] its row
+  int* row_off;  // [rows+1] first completion position of each row
+  float* lse_out;  // [rows*T] nullable; zeroed at mask-0 positions
+};
+
+struct FwdArgs {
+  const uint16_t* hidden;  // [rows*T, H]
+  const uint16_t* w;       // [V, H]
+  int H, V, Mp, gm;
+  const int* idx;
+  const int* tgt_c;
+  const WsHeader* hdr;
+  float2* part;      // [nVt, Mp] per-tile (max, sum exp)
+  float* tgt_logit;  // [Mp]
+};
+
+struct CombineArgs {
+  const float2* part;
+  const float* tgt_logit;
+  const int* tgt_c;
+  const int* idx;
+  const WsHeader* hdr;
+  int Mp, nVt;
+  double* lse64;   // [Mp]
+  double* logp64;  // [Mp]
+  float* lse_out;  // [rows*T] nullable
+};
+
+struct RowSumArgs {
+  const double* logp64;
+  const int* row_off;
+  const WsHeader* hdr;
+  int rows;
+  float* sum32;     // nullable
+  double* sum64;    // nullable
+  int32_t* n_tokens;  // nullable
+};
+
+struct TransposeWArgs {
+  const uint16_t* w;
+  int V, H, Vp;
+  uint16_t* wt;  // [H, Vp]
+};
+
+struct GatherHTArgs {
+  const uint16_t* hidden;
+  const int* idx;
+  const WsHeader* hdr;
+  int H, Mp;
+  uint16_t* ht;  // [H, Mp]
+};
+
+struct DProdArgs {
+  const uint16_t* hidden;
+  const uint16_t* w;
+  int H, V, Vp, Mp, gm;
+  const int* idx;
+  const int* tgt_c;
+  const int* row_c;
+  const WsHeader* hdr;
+  const float* lse;     // [rows*T] from the forward
+  const float* weight;  // [rows]
+  uint16_t* D;          // [Mp, Vp] bf16
+  uint16_t* DT;         // [Vp, Mp] bf16
+};
+
+struct DhArgs {
+  const uint16_t* D;
+  const uint16_t* wt;
+  int H, Vp, Mp, gm;
+  const int* idx;
+  const WsHeader* hdr;
+  float* d_hidden;  // [rows*T, H]
+};
+
+struct DwArgs {
+  const uint16_t* DT;
+  const uint16_t* ht;
+  int V, H, Vp, Mp, gm, accumulate;
+  const WsHeader* hdr;
+  float* d_w;  // [V, H]
+};
+
+struct ZeroRowsArgs {
+  const uint8_t* mask;
+  int H;
+  float* d_hidden;
+};
+
+struct StreamFwdArgs {
+  const uint16_t* logits;  // [rows*T, V]
+  int V;
+  const int* idx;
+  const int* tgt_c;
+  const WsHeader* hdr;
+  double* lse64;
+  double* logp64;
+  float* lse_out;  // nullable
+};
+
+struct StreamBwdArgs {
+  const uint16_t* logits;
+  const int32_t* targets;
+  const uint8_t* mask;
+  int T, V;
+  const float* lse;     // [rows*T]
+  const float* weight;  // [rows]
+  WsHeader* hdr;
+  uint16_t* d_logits;   // [rows*T, V]
+};
+
+struct LossArgs {
+  const double* policy;  // [2B]
+  const float* ref;      // [2B]
+  int num_pairs, layout;
+  double beta;
+  float* loss;      // [1]
+  float* weight;    // [2B]
+  float* reward;    // [2B] nullable
+  float* margin;    // [B] nullable
+  float* accuracy;  // [1] nullable
+};
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+hipError_t launch_fwd_gemm(const FwdArgs& a, int grid, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_row_sums(const RowSumArgs& a, hipStream_t s);
+hipError_t launch_transpose_w(const TransposeWArgs& a, hipStream_t s);
+hipError_t launch_gather_ht(const GatherHTArgs& a, hipStream_t s);
+hipError_t launch_dprod_gemm(const DProdArgs& a, int grid, hipStream_t s);
+hipError_t launch_dh_gemm(const DhArgs& a, int grid, hipStream_t s);
+hipError_t launch_dw_gemm(const DwArgs& a, int grid, hipStream_t s);
+hipError_t launch_zero_rows(const ZeroRowsArgs& a, long positions, hipStream_t s);
+hipError_t launch_stream_fwd(const StreamFwdArgs& a, long positions, hipStream_t s);
+hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, hipStream_t s);
+hipError_t launch_reset_status(WsHeader* hdr, hipStream_t s);
+hipError_t launch_loss(const LossArgs& a, hipStream_t s);
+
+}  // namespace dpo

@@ -1,0 +1,119 @@
+"""The C ABI on the host: the library loads, exports everything the header
+declares, and rejects bad arguments before touching a device."""
+import math
+import os
+import re
+
+import pytest
+
+from preference_alignment_amd import build as B
+from preference_alignment_amd import dpo_head as D
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        B.build()
+    return D.lib()
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def test_exports_every_declared_function(L):
+    names = D.declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_workspace_sizes(L):
+    ok = D.dpo_workspace_bytes(D.DPO_OP_SEQ_LOGPS, 8, 2048, 4096, 128256)
+    assert ok > 0
+    for args in [(3, 2048, 4096, 128256), (0, 8, 64, 64), (8, 0, 64, 64), (8, 8, 100, 64), (8, 8, 64, 1001),
+                 (8, 8, 0, 64)]:
+        assert D.dpo_workspace_bytes(D.DPO_OP_SEQ_LOGPS, *args) == 0, args
+    assert D.dpo_workspace_bytes(99, 8, 8, 64, 64) == 0
+    # logits ops ignore H
+    assert D.dpo_workspace_bytes(D.DPO_OP_LOGITS_SEQ_LOGPS, 8, 2048, 0, 128256) > 0
+    assert D.dpo_workspace_bytes(D.DPO_OP_LOGITS_BACKWARD, 8, 2048, 0, 128256) == 256
+    # the backward holds D and D^T in bf16: at least 2 * 2 * (rows*T) * V bytes
+    bw = D.dpo_workspace_bytes(D.DPO_OP_HEAD_BACKWARD, 8, 2048, 4096, 128256)
+    assert bw >= 4 * 8 * 2048 * 128256
+    # more rows never need less
+    assert D.dpo_workspace_bytes(0, 16, 2048, 4096, 128256) > ok
+
+
+def test_seq_logps_validation(L):
+    f = L.dpo_seq_logps
+    ws = D.dpo_workspace_bytes(0, 4, 64, 256, 1024)
+    good = [FAKE, FAKE, FAKE, FAKE, 4, 64, 256, 1024, FAKE, None, None, None, FAKE, ws, None]
+    assert f(*[None] + good[1:]) == D.DPO_ERR_NULL
+    bad = list(good)
+    bad[12] = None
+    assert f(*bad) == D.DPO_ERR_NULL
+    for i, v in [(4, 3), (5, 0), (6, 100), (7, 1001)]:
+        bad = list(good)
+        bad[i] = v
+        assert f(*bad) == D.DPO_ERR_SHAPE, (i, v)
+    bad = list(good)
+    bad[0] = FAKE + 2
+    assert f(*bad) == D.DPO_ERR_ALIGN
+    bad = list(good)
+    bad[13] = ws - 1
+    assert f(*bad) == D.DPO_ERR_WORKSPACE
+
+
+def test_loss_validation(L):
+    f = L.dpo_loss
+    for beta in (0.0, -0.5, math.nan, math.inf):
+        assert f(FAKE, FAKE, 2, beta, 0, FAKE, FAKE, None, None, None, None) == D.DPO_ERR_BETA
+    assert f(FAKE, FAKE, 2, 0.1, 2, FAKE, FAKE, None, None, None, None) == D.DPO_ERR_LAYOUT
+    assert f(FAKE, FAKE, 0, 0.1, 0, FAKE, FAKE, None, None, None, None) == D.DPO_ERR_SHAPE
+    assert f(None, FAKE, 2, 0.1, 0, FAKE, FAKE, None, None, None, None) == D.DPO_ERR_NULL
+
+
+def test_backward_and_logits_validation(L):
+    ws = D.dpo_workspace_bytes(2, 4, 64, 256, 1024)
+    args = [FAKE, FAKE, FAKE, FAKE, 4, 64, 256, 1024, FAKE, FAKE, FAKE, FAKE, 2, FAKE, ws, None]
+    assert L.dpo_head_backward(*args) == D.DPO_ERR_LAYOUT
+    args[12] = 0
+    args[14] = ws - 256
+    assert L.dpo_head_backward(*args) == D.DPO_ERR_WORKSPACE
+    args[10] = None
+    assert L.dpo_head_backward(*args) == D.DPO_ERR_NULL
+    wsl = D.dpo_workspace_bytes(3, 4, 64, 0, 1024)
+    assert L.dpo_logits_seq_logps(FAKE, FAKE, FAKE, 4, 64, 1020, FAKE, None, None, None, FAKE, wsl,
+                                  None) == D.DPO_ERR_SHAPE
+    assert L.dpo_logits_backward(FAKE, FAKE, FAKE, 4, 64, 1024, FAKE, FAKE, FAKE + 8, FAKE, 256,
+                                 None) == D.DPO_ERR_ALIGN
+
+
+def test_strerror_and_profile_api(L):
+    for code in range(-8, 1):
+        assert len(D.dpo_strerror(code)) >= 2
+    assert "unknown" in D.dpo_strerror(-99)
+    D.dpo_profile_enable(True)
+    assert D.dpo_profile_read() == {}
+    D.dpo_profile_enable(False)
+    assert L.dpo_profile_entry(0, None, None, None) == D.DPO_ERR_SHAPE
+
+
+def test_binding_rejects_host_tensors(L):
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(2, 4, 64, dtype=torch.bfloat16)
+    w = torch.zeros(8, 64, dtype=torch.bfloat16)
+    t = torch.zeros(2, 4, dtype=torch.int32)
+    m = torch.zeros(2, 4, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        D.dpo_seq_logps(x, w, t, m, torch.zeros(2), workspace=torch.zeros(10, dtype=torch.uint8))
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The package and its binding never import the oracle."""
+    pkg = os.path.dirname(D.__file__)
+    for root, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(root, fn)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle|import_module\(.oracle", txt, re.M), fn
