@@ -28,6 +28,7 @@ struct Layout {
   size_t hdr = 0, idx = 0, tgt = 0, rowc = 0, rowoff = 0;
   size_t part = 0, tlogit = 0, lse64 = 0, logp64 = 0;
   size_t D = 0, DT = 0, WT = 0, HT = 0;
+  size_t keysA = 0, valsA = 0, keysB = 0, valsB = 0, counters = 0;
   size_t total = 0;
 };
 
@@ -74,6 +75,11 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     L.DT = take((size_t)L.Vp * L.Mp * 2);
     L.WT = take((size_t)H * L.Vp * 2);
     L.HT = take((size_t)H * L.Mp * 2);
+    L.keysA = take((size_t)L.Mp * 4);
+    L.valsA = take((size_t)L.Mp * 4);
+    L.keysB = take((size_t)L.Mp * 4);
+    L.valsB = take((size_t)L.Mp * 4);
+    L.counters = take((size_t)kSortThreads * 256 * 4);
   }
   L.total = o;
   return L;
@@ -366,11 +372,15 @@ int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int
   DhArgs dh;
   dh.D = D;
   dh.wt = WT;
+  dh.w = w_vocab;
   dh.H = H;
   dh.Vp = L.Vp;
   dh.Mp = L.Mp;
   dh.gm = kGroupBwd;
   dh.idx = dp.idx;
+  dh.tgt_c = dp.tgt_c;
+  dh.row_c = dp.row_c;
+  dh.weight = weight;
   dh.hdr = hdr;
   dh.d_hidden = d_hidden;
   RUN("dhidden_gemm", launch_dh_gemm(dh, persistent_grid(), st));
@@ -390,6 +400,32 @@ int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int
   dw.hdr = hdr;
   dw.d_w = d_w_vocab;
   RUN("dw_gemm", launch_dw_gemm(dw, persistent_grid(), st));
+
+  // one-hot term of dW_vocab: sort positions by target, subtract per-target sums
+  int bits = 1;
+  while (bits < 31 && (1 << bits) < V) ++bits;
+  SortArgs so;
+  so.tgt_c = dp.tgt_c;
+  so.hdr = hdr;
+  so.passes = (bits + 7) / 8;
+  so.keysA = at<int>(ws, L.keysA);
+  so.valsA = at<int>(ws, L.valsA);
+  so.keysB = at<int>(ws, L.keysB);
+  so.valsB = at<int>(ws, L.valsB);
+  so.counters = at<int>(ws, L.counters);
+  RUN("sort_targets", launch_sort_targets(so, st));
+  OnehotDwArgs oh;
+  oh.keys = (so.passes & 1) ? so.keysB : so.keysA;
+  oh.vals = (so.passes & 1) ? so.valsB : so.valsA;
+  oh.idx = dp.idx;
+  oh.row_c = dp.row_c;
+  oh.weight = weight;
+  oh.hidden = hidden;
+  oh.hdr = hdr;
+  oh.H = H;
+  oh.V = V;
+  oh.d_w = d_w_vocab;
+  RUN("onehot_dw", launch_onehot_dw(oh, L.Mp, st));
   return DPO_OK;
 }
 

@@ -19,9 +19,16 @@
 //   k_row_sums       fp64 per-row sums in a fixed order
 //   k_transpose_w    W^T (bf16) for the dHidden contraction
 //   k_gather_ht      Hc^T (bf16) for the dW contraction
-//   k_dprod_gemm     recompute Z tile; epilogue D = w (exp(z - lse) - onehot) -> bf16 D, D^T
-//   k_dh_gemm        dHidden rows = D . W, scattered to their positions
+//   k_dprod_gemm     recompute Z tile; epilogue D = w exp(z - lse) -> bf16 D, D^T (softmax part)
+//   k_dh_gemm        dHidden rows = D . W - w W[target], scattered to their positions
 //   k_dw_gemm        dW_vocab = D^T . Hc (overwrite or accumulate)
+//   k_sort_targets   completion positions stably sorted by target id
+//   k_onehot_dw      dW_vocab[y] -= sum of w h over the positions whose target is y
+//
+// The one-hot term of dlogits is kept out of the bf16 operand D: rounding the
+// single large entry w (p_y - 1) to bf16 alone would cost ~1e-3 relative error
+// in dHidden.  It is applied exactly in fp32 instead, by a gather of W[y] in
+// the dHidden epilogue and a fixed-order per-target sum for dW_vocab.
 //   k_zero_rows      dHidden = 0 at positions outside the completion mask
 #include "dpo_common.h"
 #include "gemm_core.h"
@@ -243,9 +250,8 @@ __global__ __launch_bounds__(256) void k_gather_ht(GatherHTArgs a) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NTHREADS, 1) void k_dprod_gemm(DProdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  int* tgt_s = (int*)(smem + PIPE_BYTES);
-  float* lse_s = (float*)(smem + PIPE_BYTES + 1024);
-  float* w_s = (float*)(smem + PIPE_BYTES + 2048);
+  float* lse_s = (float*)(smem + PIPE_BYTES);
+  float* w_s = (float*)(smem + PIPE_BYTES + 1024);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -269,7 +275,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_dprod_gemm(DProdArgs a) {
     {
       const int m = m0 + tid;
       const bool live = m < n_c;
-      tgt_s[tid] = live ? a.tgt_c[m] : -1;
       lse_s[tid] = live ? a.lse[a.idx[m]] * kLog2e : 0.f;
       w_s[tid] = live ? a.weight[a.row_c[m]] : 0.f;
     }
@@ -285,15 +290,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_dprod_gemm(DProdArgs a) {
         for (int s = 0; s < 4; ++s) {
           const int e = q * 4 + s;
           const int row = acc_row(wm, i, e, lane);
-          const int tg = tgt_s[row];
           const float L = lse_s[row];
           const float wr = w_s[row];
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const int col = n0 + acc_col(wn, j, lane);
             const float p = fast_exp2(fmaf(acc.c[i][j][e], kLog2e, -L));
-            float dv = wr * (p - (col == tg ? 1.f : 0.f));
-            dv = col < a.V ? dv : 0.f;
+            const float dv = col < a.V ? wr * p : 0.f;
             d[j][s] = dv;
             const int m = m0 + row;
             a.D[(size_t)m * a.Vp + col] = (uint16_t)(pack_bf16x2(dv, 0.f) & 0xffffu);
@@ -348,10 +351,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_dh_gemm(DhArgs a) {
         const int m = m0 + acc_row(wm, i, e, lane);
         if (m >= n_c) continue;
         float* dst = a.d_hidden + (size_t)a.idx[m] * a.H;
+        const int tg = a.tgt_c[m];
+        const float wr = tg >= 0 ? a.weight[a.row_c[m]] : 0.f;
+        const uint16_t* wrow = a.w + (size_t)(tg >= 0 ? tg : 0) * a.H;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = n0 + acc_col(wn, j, lane);
-          if (col < a.H) dst[col] = acc.c[i][j][e];
+          if (col < a.H) dst[col] = fmaf(-wr, bf16_bits_to_float(wrow[col]), acc.c[i][j][e]);
         }
       }
     }
@@ -402,6 +408,121 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_dw_gemm(DwArgs a) {
       }
     }
     __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// one-hot term of dW_vocab: positions sorted by target, then a fixed-order sum
+// ---------------------------------------------------------------------------
+// Stable LSD radix sort (8-bit digits) of the completion positions by target
+// id, in one workgroup.  Each thread owns a contiguous slice of the input, so
+// counting and scattering slice by slice in digit-major order keeps equal
+// keys in ascending position order.  Out-of-range targets (-1) sort last.
+__global__ __launch_bounds__(kSortThreads) void k_sort_targets(SortArgs a) {
+  __shared__ int dig_base[256];
+  __shared__ int dig_tot[256];
+  const int n = a.hdr->n_c;
+  const int tid = threadIdx.x;
+  const int per = cdiv(n, kSortThreads);
+  const int lo = min(n, per * tid), hi = min(n, lo + per);
+  int* cnt = a.counters + tid * 256;
+  const int* kin = a.tgt_c;
+  const int* vin = nullptr;
+  int* kout = a.keysB;
+  int* vout = a.valsB;
+  for (int p = 0; p < a.passes; ++p) {
+    const int shift = 8 * p;
+    for (int d = 0; d < 256; ++d) cnt[d] = 0;
+    for (int i = lo; i < hi; ++i) cnt[((unsigned)kin[i] >> shift) & 255u] += 1;
+    __syncthreads();
+    if (tid < 256) {
+      int run = 0;
+      for (int t = 0; t < kSortThreads; ++t) {
+        int* c = a.counters + t * 256 + tid;
+        const int v = *c;
+        *c = run;
+        run += v;
+      }
+      dig_tot[tid] = run;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int d = 0; d < 256; ++d) {
+        dig_base[d] = run;
+        run += dig_tot[d];
+      }
+    }
+    __syncthreads();
+    for (int i = lo; i < hi; ++i) {
+      const int k = kin[i];
+      const int d = ((unsigned)k >> shift) & 255u;
+      const int o = dig_base[d] + cnt[d]++;
+      kout[o] = k;
+      vout[o] = vin ? vin[i] : i;
+    }
+    __syncthreads();
+    kin = kout;
+    vin = vout;
+    kout = (kout == a.keysB) ? a.keysA : a.keysB;
+    vout = (vout == a.valsB) ? a.valsA : a.valsB;
+  }
+}
+
+// Each block takes 64 consecutive entries of the sorted list and, for every
+// run of equal targets that starts there, subtracts sum_t w_t h_t (ascending t)
+// from that dW_vocab row, 1024 columns per block (4 per thread).
+constexpr int kOnehotChunk = 64;
+constexpr int kOnehotCols = 1024;
+
+__global__ __launch_bounds__(256) void k_onehot_dw(OnehotDwArgs a) {
+  const int n = a.hdr->n_c;
+  const int i0 = blockIdx.x * kOnehotChunk;
+  const int c0 = blockIdx.y * kOnehotCols + threadIdx.x * 4;
+  if (i0 >= n || c0 >= a.H) return;
+  const int i1 = min(n, i0 + kOnehotChunk);
+  for (int i = i0; i < i1; ++i) {
+    const int k = a.keys[i];
+    if ((i > 0 && a.keys[i - 1] == k) || k < 0 || k >= a.V) continue;
+    int e = i + 1;
+    while (e < n && a.keys[e] == k) ++e;
+    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+    int j = i;
+    for (; j + 4 <= e; j += 4) {
+      int mm[4];
+      float ww[4];
+      uint2 hh[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mm[u] = a.vals[j + u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ww[u] = a.weight[a.row_c[mm[u]]];
+        hh[u] = *(const uint2*)(a.hidden + (size_t)a.idx[mm[u]] * a.H + c0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc0 = fmaf(ww[u], bf16_lo(hh[u].x), acc0);
+        acc1 = fmaf(ww[u], bf16_hi(hh[u].x), acc1);
+        acc2 = fmaf(ww[u], bf16_lo(hh[u].y), acc2);
+        acc3 = fmaf(ww[u], bf16_hi(hh[u].y), acc3);
+      }
+    }
+    for (; j < e; ++j) {
+      const int m = a.vals[j];
+      const float w = a.weight[a.row_c[m]];
+      const uint2 h = *(const uint2*)(a.hidden + (size_t)a.idx[m] * a.H + c0);
+      acc0 = fmaf(w, bf16_lo(h.x), acc0);
+      acc1 = fmaf(w, bf16_hi(h.x), acc1);
+      acc2 = fmaf(w, bf16_lo(h.y), acc2);
+      acc3 = fmaf(w, bf16_hi(h.y), acc3);
+    }
+    float4* dst = (float4*)(a.d_w + (size_t)k * a.H + c0);
+    float4 v = *dst;
+    v.x -= acc0;
+    v.y -= acc1;
+    v.z -= acc2;
+    v.w -= acc3;
+    *dst = v;
   }
 }
 
@@ -472,6 +593,16 @@ hipError_t launch_dw_gemm(const DwArgs& a, int grid, hipStream_t s) {
   static hipError_t once = prep_gemm((const void*)k_dw_gemm);
   if (once != hipSuccess) return once;
   hipLaunchKernelGGL(k_dw_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_targets(const SortArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_sort_targets, dim3(1), dim3(kSortThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_onehot_dw(const OnehotDwArgs& a, int Mp, hipStream_t s) {
+  hipLaunchKernelGGL(k_onehot_dw, dim3(Mp / kOnehotChunk, cdiv(a.H, kOnehotCols)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

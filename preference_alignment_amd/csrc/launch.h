@@ -86,10 +86,37 @@ struct DProdArgs {
 struct DhArgs {
   const uint16_t* D;
   const uint16_t* wt;
+  const uint16_t* w;    // [V, H] for the exact one-hot term
   int H, Vp, Mp, gm;
   const int* idx;
+  const int* tgt_c;
+  const int* row_c;
+  const float* weight;  // [rows]
   const WsHeader* hdr;
   float* d_hidden;  // [rows*T, H]
+};
+
+struct SortArgs {
+  const int* tgt_c;     // [n_c] keys in position order
+  const WsHeader* hdr;
+  int passes;           // 8-bit digits needed to cover V
+  int* keysA;
+  int* valsA;
+  int* keysB;
+  int* valsB;
+  int* counters;        // [kSortThreads * 256]
+};
+
+struct OnehotDwArgs {
+  const int* keys;      // [n_c] targets, sorted
+  const int* vals;      // [n_c] compact positions, ascending within a target
+  const int* idx;
+  const int* row_c;
+  const float* weight;
+  const uint16_t* hidden;
+  const WsHeader* hdr;
+  int H, V;
+  float* d_w;
 };
 
 struct DwArgs {
@@ -150,6 +177,9 @@ hipError_t launch_dprod_gemm(const DProdArgs& a, int grid, hipStream_t s);
 hipError_t launch_dh_gemm(const DhArgs& a, int grid, hipStream_t s);
 hipError_t launch_dw_gemm(const DwArgs& a, int grid, hipStream_t s);
 hipError_t launch_zero_rows(const ZeroRowsArgs& a, long positions, hipStream_t s);
+hipError_t launch_sort_targets(const SortArgs& a, hipStream_t s);
+hipError_t launch_onehot_dw(const OnehotDwArgs& a, int Mp, hipStream_t s);
+constexpr int kSortThreads = 512;
 hipError_t launch_stream_fwd(const StreamFwdArgs& a, long positions, hipStream_t s);
 hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, hipStream_t s);
 hipError_t launch_reset_status(WsHeader* hdr, hipStream_t s);

@@ -126,7 +126,9 @@ def test_accumulate_dw_adds():
     weight = torch.linspace(-0.05, 0.05, x.rows, dtype=torch.float32, device=dev)
     _, dw1 = run_backward(x, d, g["lse"], weight, dev)
     _, dw2 = run_backward(x, d, g["lse"], weight, dev, d_w=dw1.clone(), accumulate=1)
-    assert torch.equal(dw2, dw1 + dw1)
+    # the softmax part is added to the old values and the one-hot part applied
+    # after it, so the sum equals dw1 + dw1 up to fp32 rounding
+    assert float((dw2 - 2 * dw1).abs().max()) <= 1e-6 * float(dw1.abs().max())
 
 
 def test_run_to_run_bitwise_deterministic():
