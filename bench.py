@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=256)
     p.add_argument("--no-kernel-timing", action="store_true")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of this many MiB (5 times), to scale "
+                        "hardware byte counters")
     return p.parse_args()
 
 
@@ -155,9 +158,9 @@ def cpu_baseline(x, k, sample_tokens):
         what = "fwd"
     else:
         fwd = O.seq_logps(x.hidden[rows], x.w_vocab, tg, mask)
-        O.head_step(x.hidden[rows], x.w_vocab, tg, mask, fwd["logp_sum"] + x.ref_noise[rows], x.beta,
-                    x.layout)
-        what = "fwd+loss+bwd (head_step includes its own forward)"
+        loss = O.dpo_loss(fwd["logp_sum"], fwd["logp_sum"] + x.ref_noise[rows], x.beta, x.layout)
+        O.head_backward(x.hidden[rows], x.w_vocab, tg, mask, fwd["lse"], loss["weight"])
+        what = "fwd+loss+bwd"
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "completion tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first pair, {sample_tokens} completion positions per row ({n} tokens), "
@@ -174,6 +177,15 @@ def main():
     from preference_alignment_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    if a.copy_calibration:
+        n = a.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
     D.lib()  # fail loudly if the HIP library is missing
     x = W.make_workload(a.workload)
     n_c = x.n_completion
