@@ -9,7 +9,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/dpo_head.h"
+#include "dpo_head.h"
 #include "dpo_common.h"
 #include "gemm_core.h"
 #include "launch.h"
@@ -17,6 +17,13 @@
 using namespace dpo;
 
 namespace {
+
+// Tile-group widths (m-tiles per group) of the persistent scheduler.
+constexpr int kGroupFwd = 8;
+constexpr int kGroupBwd = 4;
+// The dHidden contraction has few output tiles (positions x H); splitting its
+// K = vocabulary range in two keeps every CU busy through the last round.
+constexpr int kSplitDh = 2;
 
 // ---------------------------------------------------------------------------
 // workspace layout
@@ -28,7 +35,7 @@ struct Layout {
   size_t hdr = 0, idx = 0, tgt = 0, rowc = 0, rowoff = 0;
   size_t part = 0, tlogit = 0, lse64 = 0, logp64 = 0;
   size_t D = 0, DT = 0, WT = 0, HT = 0;
-  size_t keysA = 0, valsA = 0, keysB = 0, valsB = 0, counters = 0;
+  size_t keysA = 0, valsA = 0, keysB = 0, valsB = 0, counters = 0, dhpart = 0;
   size_t total = 0;
 };
 
@@ -80,6 +87,7 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     L.keysB = take((size_t)L.Mp * 4);
     L.valsB = take((size_t)L.Mp * 4);
     L.counters = take((size_t)kSortThreads * 256 * 4);
+    L.dhpart = take((size_t)kSplitDh * L.Mp * H * 4);
   }
   L.total = o;
   return L;
@@ -108,9 +116,6 @@ int persistent_grid() {
   return cus[dev];
 }
 
-// Tile-group widths (m-tiles per group) of the persistent scheduler.
-constexpr int kGroupFwd = 8;
-constexpr int kGroupBwd = 4;
 
 // ---------------------------------------------------------------------------
 // kernel timing
@@ -372,18 +377,27 @@ int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int
   DhArgs dh;
   dh.D = D;
   dh.wt = WT;
-  dh.w = w_vocab;
   dh.H = H;
   dh.Vp = L.Vp;
   dh.Mp = L.Mp;
   dh.gm = kGroupBwd;
-  dh.idx = dp.idx;
-  dh.tgt_c = dp.tgt_c;
-  dh.row_c = dp.row_c;
-  dh.weight = weight;
+  dh.splitk = kSplitDh;
   dh.hdr = hdr;
-  dh.d_hidden = d_hidden;
+  dh.part = at<float>(ws, L.dhpart);
   RUN("dhidden_gemm", launch_dh_gemm(dh, persistent_grid(), st));
+  DhFinishArgs df;
+  df.part = dh.part;
+  df.w = w_vocab;
+  df.idx = dp.idx;
+  df.tgt_c = dp.tgt_c;
+  df.row_c = dp.row_c;
+  df.weight = weight;
+  df.hdr = hdr;
+  df.H = H;
+  df.Mp = L.Mp;
+  df.splitk = kSplitDh;
+  df.d_hidden = d_hidden;
+  RUN("dhidden_finish", launch_dh_finish(df, L.Mp, st));
 
   ZeroRowsArgs z{mask, H, d_hidden};
   RUN("zero_rows", launch_zero_rows(z, (long)rows * T, st));

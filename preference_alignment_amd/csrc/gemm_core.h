@@ -7,17 +7,23 @@
 //   dHidden             : A = D (dlogits, bf16), B = W_vocab^T
 //   dW_vocab            : A = D^T,              B = hidden^T at completion positions
 //
-// Block tile 256x256x64, 256 threads = 4 waves in a 2x2 grid, each wave owns a
-// 128x128 sub-tile held as 4x4 fragments of v_mfma_f32_32x32x16_bf16.
-// Operand tiles go from global memory straight into LDS with
-// global_load_lds_dwordx4 (16 bytes per lane, no register staging), double
-// buffered (2 stages x 2 operands x 32 KiB = 128 KiB of the 160 KiB LDS).
+// Block tile 256x256x64, 512 threads = 8 waves in a 2x4 grid (two waves per
+// SIMD, so one wave's LDS and barrier waits are covered by the other's MFMAs);
+// each wave owns a 128x64 sub-tile held as 4x2 fragments of
+// v_mfma_f32_32x32x16_bf16 (128 accumulator registers).  Operand tiles go
+// from global memory straight into LDS with global_load_lds_dwordx4 (16 bytes
+// per lane, no register staging), double buffered (2 stages x 2 operands x
+// 32 KiB = 128 KiB of the 160 KiB LDS).  The K loop is software pipelined:
+// the fragments of the next 16-wide K step are read while the MFMAs of the
+// current one issue, and the stage barrier sits inside the MFMA stream of the
+// last step of a stage, with the next stage's first fragments read across it.
 //
 // LDS layout of one operand tile: 256 rows x 128 bytes (64 bf16 of K).  The
 // 16-byte chunk c of row r is stored at chunk position c ^ ((r >> 1) & 7) so
-// that the fragment reads (32 rows, same logical chunk) spread over all banks.
-// global_load_lds places lane L's 16 bytes at (wave base + 16 L), so the
-// swizzle is realised by choosing which global chunk each lane fetches.
+// that the fragment reads (32 rows, same logical chunk) spread over all banks
+// (no bank conflicts measured).  global_load_lds places lane L's 16 bytes at
+// (wave base + 16 L), so the swizzle is realised by choosing which global
+// chunk each lane fetches.
 //
 // MFMA 32x32x16 register layout (CDNA3/CDNA4 32x32 family): lane l supplies
 // A[l % 32][8 (l / 32) + 0..7] and B^T likewise; accumulator element e of lane
@@ -34,13 +40,16 @@ namespace gemm {
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int NTHREADS = 256;
-constexpr int FM = 4;  // 32-row fragments per wave
-constexpr int FN = 4;  // 32-col fragments per wave
+constexpr int NTHREADS = 512;
+constexpr int WAVES_N = 4;             // waves along the MFMA columns
+constexpr int FM = 4;                  // 32-row fragments per wave (128 rows)
+constexpr int FN = 2;                  // 32-col fragments per wave (64 cols)
+constexpr int WAVE_COLS = 32 * FN;
 constexpr int OPER_BYTES = BM * BK * 2;       // 32 KiB
 constexpr int STAGE_BYTES = 2 * OPER_BYTES;   // A + B
 constexpr int PIPE_BYTES = 2 * STAGE_BYTES;   // double buffer, 128 KiB
-constexpr int LOADS_PER_THREAD = BM * (BK / 8) / NTHREADS;  // 8 rows per operand
+constexpr int LOADS_PER_THREAD = BM * (BK / 8) / NTHREADS;  // 4 rows per operand
+constexpr int LOADER_ROW_STRIDE = NTHREADS / 8;             // 64
 constexpr int NUM_XCD = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -50,8 +59,8 @@ struct Acc {
 };
 
 // Per-thread constants of the loader: this thread fetches rows
-// (it * 32 + tid / 8), it = 0..7, at logical chunk lchunk() of each K step.
-__device__ __forceinline__ int loader_row(int it, int tid) { return it * 32 + (tid >> 3); }
+// (it * 64 + tid / 8), it = 0..3, at logical chunk lchunk() of each K step.
+__device__ __forceinline__ int loader_row(int it, int tid) { return it * LOADER_ROW_STRIDE + (tid >> 3); }
 __device__ __forceinline__ int loader_lchunk(int tid) { return (tid & 7) ^ ((tid >> 4) & 7); }
 
 // Issue the global->LDS copies of one operand tile for one K step.
@@ -67,11 +76,16 @@ __device__ __forceinline__ void load_tile(const uint16_t* const (&rows)[LOADS_PE
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// The K loop.  nk = number of BK steps (may be 0: accumulators stay zero).
-// The caller guarantees every row pointer is valid for k < nk * BK.
+// The K loop over [k_begin, k_begin + nk*BK).  nk may be 0 (accumulators stay
+// zero).  The caller guarantees every row pointer is valid over that range.
+// SWAP = false: MFMA rows come from the first operand tile (arows) and
+// columns from the second (brows).  SWAP = true: the roles are exchanged, so
+// accumulator rows index the second operand and columns the first.
+// Wave (wm, wn) owns MFMA rows wm*128 .. +128 and columns wn*64 .. +64.
+template <bool SWAP>
 __device__ __forceinline__ void mainloop(Acc& acc, const uint16_t* const (&arows)[LOADS_PER_THREAD],
-                                         const uint16_t* const (&brows)[LOADS_PER_THREAD], int nk,
-                                         char* smem, int wave, int lane, int wm, int wn) {
+                                         const uint16_t* const (&brows)[LOADS_PER_THREAD], int k_begin,
+                                         int nk, char* smem, int wave, int lane, int wm, int wn) {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -82,42 +96,78 @@ __device__ __forceinline__ void mainloop(Acc& acc, const uint16_t* const (&arows
 
   // fragment read offsets (bytes) inside an operand tile
   const int sw = (lane >> 1) & 7;
-  const int a_off = (wm * 128 + (lane & 31)) * 128;
-  const int b_off = (wn * 128 + (lane & 31)) * 128;
+  const int r_off = (wm * 128 + (lane & 31)) * 128 + (SWAP ? OPER_BYTES : 0);       // MFMA-row fragments
+  const int c_off = (wn * WAVE_COLS + (lane & 31)) * 128 + (SWAP ? 0 : OPER_BYTES);  // MFMA-column fragments
   int choff[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) choff[kk] = (((2 * kk + (lane >> 5)) ^ sw) << 4);
 
-  load_tile(arows, 0, smem, wave);
-  load_tile(brows, 0, smem + OPER_BYTES, wave);
+  bf16x8_t fa[2][FM], fb[2][FN];
+#define DPO_READ_FRAGS(stage_, kk_, slot_)                                                     \
+  do {                                                                                         \
+    const char* base_ = smem + (stage_) * STAGE_BYTES;                                         \
+    _Pragma("unroll") for (int i_ = 0; i_ < FM; ++i_) fa[slot_][i_] =                          \
+        *(const bf16x8_t*)(base_ + r_off + i_ * 4096 + choff[kk_]);                            \
+    _Pragma("unroll") for (int j_ = 0; j_ < FN; ++j_) fb[slot_][j_] =                          \
+        *(const bf16x8_t*)(base_ + c_off + j_ * 4096 + choff[kk_]);                            \
+  } while (0)
+
+  load_tile(arows, k_begin, smem, wave);
+  load_tile(brows, k_begin, smem + OPER_BYTES, wave);
   wait_loads();
   __syncthreads();
+  if (nk > 1) {
+    load_tile(arows, k_begin + BK, smem + STAGE_BYTES, wave);
+    load_tile(brows, k_begin + BK, smem + STAGE_BYTES + OPER_BYTES, wave);
+  }
+  DPO_READ_FRAGS(0, 0, 0);
 
   for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * STAGE_BYTES;
-    if (kt + 1 < nk) {
-      char* nxt = smem + ((kt + 1) & 1) * STAGE_BYTES;
-      load_tile(arows, (kt + 1) * BK, nxt, wave);
-      load_tile(brows, (kt + 1) * BK, nxt + OPER_BYTES, wave);
-    }
-    const char* As = cur;
-    const char* Bs = cur + OPER_BYTES;
+    const int cur = kt & 1;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bf16x8_t a[FM], b[FN];
+      const int sl = kk & 1;
+      if (kk < 3) {
+        if (sl)
+          DPO_READ_FRAGS(cur, kk + 1, 0);
+        else
+          DPO_READ_FRAGS(cur, kk + 1, 1);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = *(const bf16x8_t*)(As + a_off + i * 4096 + choff[kk]);
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b[j] = *(const bf16x8_t*)(Bs + b_off + j * 4096 + choff[kk]);
+          for (int j = 0; j < FN; ++j)
+            acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][i], fb[sl][j], acc.c[i][j], 0, 0, 0);
+        // one fragment read between consecutive MFMAs
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int u = 0; u < FM + FN; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+        // last 16-wide step of the stage: 2 MFMAs, the stage barrier, the next
+        // stage's loads and first fragments, then the remaining MFMAs
+        acc.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][0], fb[1][0], acc.c[0][0], 0, 0, 0);
+        acc.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][0], fb[1][1], acc.c[0][1], 0, 0, 0);
+        if (kt + 1 < nk) {
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          if (kt + 2 < nk) {
+            load_tile(arows, k_begin + (kt + 2) * BK, smem + cur * STAGE_BYTES, wave);
+            load_tile(brows, k_begin + (kt + 2) * BK, smem + cur * STAGE_BYTES + OPER_BYTES, wave);
+          }
+          DPO_READ_FRAGS(cur ^ 1, 0, 0);
+        }
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
+        for (int u = 2; u < FM * FN; ++u)
+          acc.c[u / FN][u % FN] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][u / FN], fb[1][u % FN], acc.c[u / FN][u % FN], 0, 0, 0);
+      }
     }
-    wait_loads();
-    __syncthreads();
   }
+#undef DPO_READ_FRAGS
+  // every wave is done with the LDS tiles before the caller reuses them
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __syncthreads();
 }
 
 // Row (within the 256-row block tile) and column (within the 256-col tile) of
@@ -125,7 +175,7 @@ __device__ __forceinline__ void mainloop(Acc& acc, const uint16_t* const (&arows
 __device__ __forceinline__ int acc_row(int wm, int i, int e, int lane) {
   return wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
 }
-__device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * 128 + j * 32 + (lane & 31); }
+__device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * WAVE_COLS + j * 32 + (lane & 31); }
 
 // Persistent tile scheduler.  Tiles are numbered in grouped order (GM m-tiles
 // wide, m fastest, then n) and the numbering is cut into NUM_XCD contiguous

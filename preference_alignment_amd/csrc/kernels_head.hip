@@ -20,7 +20,8 @@
 //   k_transpose_w    W^T (bf16) for the dHidden contraction
 //   k_gather_ht      Hc^T (bf16) for the dW contraction
 //   k_dprod_gemm     recompute Z tile; epilogue D = w exp(z - lse) -> bf16 D, D^T (softmax part)
-//   k_dh_gemm        dHidden rows = D . W - w W[target], scattered to their positions
+//   k_dh_gemm        dHidden partials = D . W over vocabulary halves (split K)
+//   k_dh_finish      dHidden rows = sum of partials - w W[target], scattered to their positions
 //   k_dw_gemm        dW_vocab = D^T . Hc (overwrite or accumulate)
 //   k_sort_targets   completion positions stably sorted by target id
 //   k_onehot_dw      dW_vocab[y] -= sum of w h over the positions whose target is y
@@ -99,16 +100,32 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CompactArgs a) {
 // ---------------------------------------------------------------------------
 // forward contraction with the online log-sum-exp epilogue
 // ---------------------------------------------------------------------------
-constexpr int kEpiBytes = 8192;  // per-row staging + cross-wave reduction
+// The MFMA runs with exchanged roles (rows = vocabulary, columns = positions):
+// a lane then holds one position and 64 of the wave's 128 vocabulary entries,
+// the other 64 sitting in lane ^ 32.  The per-position max and sum of
+// exponentials over the wave's columns are in-lane reductions plus one
+// cross-half shuffle, and the two vocabulary halves of the block (wm = 0, 1)
+// meet through a small LDS table.
+constexpr int kEpiBytes = 8192;  // per-position staging + cross-wave reduction
 
-__global__ __launch_bounds__(NTHREADS, 1) void k_fwd_gemm(FwdArgs a) {
+template <typename F>
+__device__ __forceinline__ void for_vocab(const Acc& acc, int j, bool full, int vbase, int V, int lane, F f) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if (full || vbase + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3) < V) f(acc.c[i][j][e]);
+    }
+}
+
+__global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int* tgt_s = (int*)(smem + PIPE_BYTES);                  // 256 ints
   float2* red = (float2*)(smem + PIPE_BYTES + 1024);       // [2][256]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int n_c = a.hdr->n_c;
   Sched sc;
   sc.init(cdiv(n_c, BM), cdiv(a.V, BN), a.gm);
@@ -125,44 +142,43 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_fwd_gemm(FwdArgs a) {
       arows[it] = a.hidden + (size_t)a.idx[m0 + r] * a.H + lchunk * 8;
       brows[it] = a.w + (size_t)min(n0 + r, a.V - 1) * a.H + lchunk * 8;
     }
-    tgt_s[tid] = a.tgt_c[m0 + tid];
+    if (tid < BM) tgt_s[tid] = a.tgt_c[m0 + tid];
     Acc acc;
-    mainloop(acc, arows, brows, a.H / BK, smem, wave, lane, wm, wn);
+    mainloop<true>(acc, arows, brows, 0, a.H / BK, smem, wave, lane, wm, wn);
 
-    const int cbase = n0 + wn * 128;  // first column of this wave
+    const int vbase = n0 + wm * 128;  // first vocabulary row of this wave
+    const bool full = n0 + BN <= a.V;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int j = 0; j < FN; ++j) {
+      const int pl = acc_col(wn, j, lane);  // position within the tile
+      float mx = -INFINITY;
+      for_vocab(acc, j, full, vbase, a.V, lane, [&](float v) { mx = fmaxf(mx, v); });
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float ml = mx * kLog2e;
+      float s = 0.f;
+      for_vocab(acc, j, full, vbase, a.V, lane, [&](float v) { s += fast_exp2(fmaf(v, kLog2e, -ml)); });
+      s += __shfl_xor(s, 32, 64);
+      const int off = tgt_s[pl] - vbase;
+      if (off >= 0 && off < 128) {
+        const int r = off & 31;
+        if (((r >> 2) & 1) == (lane >> 5) && m0 + pl < n_c) {
+          const int ii = off >> 5, ee = ((r >> 3) << 2) | (r & 3);
+          float v = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = acc_row(wm, i, e, lane);
-        float mx = -INFINITY;
+          for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          if (cbase + j * 32 + (lane & 31) < a.V) mx = fmaxf(mx, acc.c[i][j][e]);
-        mx = half_max(mx);
-        float s = 0.f;
-        const float mxl = mx * kLog2e;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          if (cbase + j * 32 + (lane & 31) < a.V) s += fast_exp2(fmaf(acc.c[i][j][e], kLog2e, -mxl));
-        s = half_sum(s);
-        const int off = tgt_s[row] - cbase;
-        if (off >= 0 && off < 128 && (off & 31) == (lane & 31) && m0 + row < n_c) {
-          const int jj = off >> 5;
-          float v = acc.c[i][0][e];
-          v = jj == 1 ? acc.c[i][1][e] : v;
-          v = jj == 2 ? acc.c[i][2][e] : v;
-          v = jj == 3 ? acc.c[i][3][e] : v;
-          a.tgt_logit[m0 + row] = v;
+            for (int e = 0; e < 16; ++e) v = (ii == i && ee == e) ? acc.c[i][j][e] : v;
+          a.tgt_logit[m0 + pl] = v;
         }
-        if ((lane & 31) == 0) red[wn * 256 + row] = make_float2(mx, s);
       }
+      if (lane < 32) red[wm * 256 + pl] = make_float2(mx, s);
     }
     __syncthreads();
-    {
+    if (tid < BM) {
       const float2 p0 = red[tid], p1 = red[256 + tid];
       const float M = fmaxf(p0.x, p1.x);
-      const float S = p0.y * fast_exp2((p0.x - M) * kLog2e) + p1.y * fast_exp2((p1.x - M) * kLog2e);
+      const float S = (p0.x == -INFINITY ? 0.f : p0.y * fast_exp2((p0.x - M) * kLog2e)) +
+                      (p1.x == -INFINITY ? 0.f : p1.y * fast_exp2((p1.x - M) * kLog2e));
       if (m0 + tid < n_c) a.part[(size_t)nt * a.Mp + m0 + tid] = make_float2(M, S);
     }
     __syncthreads();
@@ -246,16 +262,29 @@ __global__ __launch_bounds__(256) void k_gather_ht(GatherHTArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// backward: recompute Z, D = w (exp(z - lse) - onehot) in bf16, both layouts
+// backward: recompute Z, D = w exp(z - lse) in bf16, written in both layouts
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NTHREADS, 1) void k_dprod_gemm(DProdArgs a) {
+// Same exchanged-role MFMA as the forward: a lane holds 4 consecutive
+// vocabulary entries of one position per accumulator group, packed to one
+// 8-byte LDS write.  The bf16 tile (256 positions x 256 vocabulary, 128 KiB)
+// is staged in the freed pipeline LDS and leaves as 16-byte coalesced rows of
+// D [Mp, Vp] and of D^T [Vp, Mp].  Staging layout: 16-byte chunk c of
+// position row p sits at chunk c ^ f(p), f(p) = (p ^ (p >> 3)) & 31, which
+// keeps both the row-wise writes/reads and the column-wise (transposing)
+// reads free of bank conflicts.
+__device__ __forceinline__ int stage_off(int p, int v) {
+  const int f = (p ^ (p >> 3)) & 31;
+  return p * 512 + ((((v >> 3) ^ f)) << 4) + ((v & 7) << 1);
+}
+
+__global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float* lse_s = (float*)(smem + PIPE_BYTES);
   float* w_s = (float*)(smem + PIPE_BYTES + 1024);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int n_c = a.hdr->n_c;
   Sched sc;
   sc.init(cdiv(n_c, BM), a.Vp / BN, a.gm);
@@ -272,67 +301,88 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_dprod_gemm(DProdArgs a) {
       arows[it] = a.hidden + (size_t)a.idx[m0 + r] * a.H + lchunk * 8;
       brows[it] = a.w + (size_t)min(n0 + r, a.V - 1) * a.H + lchunk * 8;
     }
-    {
+    if (tid < BM) {
       const int m = m0 + tid;
       const bool live = m < n_c;
       lse_s[tid] = live ? a.lse[a.idx[m]] * kLog2e : 0.f;
       w_s[tid] = live ? a.weight[a.row_c[m]] : 0.f;
     }
     Acc acc;
-    mainloop(acc, arows, brows, a.H / BK, smem, wave, lane, wm, wn);
+    mainloop<true>(acc, arows, brows, 0, a.H / BK, smem, wave, lane, wm, wn);
 
+    // D values (bf16) into the staging tile; the pipeline LDS is free now
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int j = 0; j < FN; ++j) {
+      const int pl = acc_col(wn, j, lane);
+      const float L = lse_s[pl];
+      const float wr = w_s[pl];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float d[FN][4];
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int e = q * 4 + s;
-          const int row = acc_row(wm, i, e, lane);
-          const float L = lse_s[row];
-          const float wr = w_s[row];
+        for (int q = 0; q < 4; ++q) {
+          const int vl = wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);  // first of 4 vocabulary rows
+          float d[4];
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int col = n0 + acc_col(wn, j, lane);
-            const float p = fast_exp2(fmaf(acc.c[i][j][e], kLog2e, -L));
-            const float dv = col < a.V ? wr * p : 0.f;
-            d[j][s] = dv;
-            const int m = m0 + row;
-            a.D[(size_t)m * a.Vp + col] = (uint16_t)(pack_bf16x2(dv, 0.f) & 0xffffu);
+          for (int u = 0; u < 4; ++u) {
+            const float p = fast_exp2(fmaf(acc.c[i][j][4 * q + u], kLog2e, -L));
+            d[u] = n0 + vl + u < a.V ? wr * p : 0.f;
           }
-        }
-        const int mrow = m0 + acc_row(wm, i, q * 4, lane);  // first of 4 consecutive rows
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + acc_col(wn, j, lane);
           uint2 pk;
-          pk.x = pack_bf16x2(d[j][0], d[j][1]);
-          pk.y = pack_bf16x2(d[j][2], d[j][3]);
-          *(uint2*)(a.DT + (size_t)col * a.Mp + mrow) = pk;
+          pk.x = pack_bf16x2(d[0], d[1]);
+          pk.y = pack_bf16x2(d[2], d[3]);
+          *(uint2*)(smem + stage_off(pl, vl)) = pk;
         }
+    }
+    __syncthreads();
+    // D rows: position m0+p, vocabulary n0 .. n0+255
+#pragma unroll 4
+    for (int it = 0; it < BM * 32 / NTHREADS; ++it) {
+      const int g = it * NTHREADS + tid;
+      const int p = g >> 5, c = g & 31;
+      const u32x4 v = *(const u32x4*)(smem + stage_off(p, c * 8));
+      *(u32x4*)(a.D + (size_t)(m0 + p) * a.Vp + n0 + c * 8) = v;
+    }
+    // D^T rows: vocabulary n0+v, positions m0 .. m0+255
+#pragma unroll 2
+    for (int it = 0; it < BN * 32 / NTHREADS; ++it) {
+      const int g = it * NTHREADS + tid;
+      const int v = g >> 5, c = g & 31;
+      uint32_t w4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t lo = *(const uint16_t*)(smem + stage_off(c * 8 + 2 * u, v));
+        const uint32_t hi = *(const uint16_t*)(smem + stage_off(c * 8 + 2 * u + 1, v));
+        w4[u] = lo | (hi << 16);
       }
+      const u32x4 o = {w4[0], w4[1], w4[2], w4[3]};
+      *(u32x4*)(a.DT + (size_t)(n0 + v) * a.Mp + m0 + c * 8) = o;
     }
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// dHidden = D . W  (A = D rows, B = W^T rows), scattered to positions
+// dHidden = D . W  (A = D rows, B = W^T rows), K = vocabulary split in `splitk`
+// parts written as fp32 partials; k_dh_finish adds them in a fixed order,
+// applies the exact one-hot term and scatters rows to their positions.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NTHREADS, 1) void k_dh_gemm(DhArgs a) {
+__global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int n_c = a.hdr->n_c;
+  const int nNt = cdiv(a.H, BN);
+  const int nkt = a.Vp / BK;
+  const int nks = cdiv(nkt, a.splitk);
   Sched sc;
-  sc.init(cdiv(n_c, BM), cdiv(a.H, BN), a.gm);
+  sc.init(cdiv(n_c, BM), nNt * a.splitk, a.gm);
   const int lchunk = loader_lchunk(tid);
   for (int t = sc.begin; t < sc.end; t += sc.step) {
-    int mt, nt;
-    sc.coords(t, mt, nt);
+    int mt, ntk;
+    sc.coords(t, mt, ntk);
+    const int nt = ntk % nNt, ks = ntk / nNt;
     const int m0 = mt * BM, n0 = nt * BN;
     const uint16_t* arows[LOADS_PER_THREAD];
     const uint16_t* brows[LOADS_PER_THREAD];
@@ -342,22 +392,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_dh_gemm(DhArgs a) {
       arows[it] = a.D + (size_t)(m0 + r) * a.Vp + lchunk * 8;
       brows[it] = a.wt + (size_t)min(n0 + r, a.H - 1) * a.Vp + lchunk * 8;
     }
+    const int kb = ks * nks;
+    const int nk = max(0, min(nks, nkt - kb));
     Acc acc;
-    mainloop(acc, arows, brows, a.Vp / BK, smem, wave, lane, wm, wn);
+    mainloop<false>(acc, arows, brows, kb * BK, nk, smem, wave, lane, wm, wn);
+    float* part = a.part + (size_t)ks * a.Mp * a.H;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int m = m0 + acc_row(wm, i, e, lane);
         if (m >= n_c) continue;
-        float* dst = a.d_hidden + (size_t)a.idx[m] * a.H;
-        const int tg = a.tgt_c[m];
-        const float wr = tg >= 0 ? a.weight[a.row_c[m]] : 0.f;
-        const uint16_t* wrow = a.w + (size_t)(tg >= 0 ? tg : 0) * a.H;
+        float* dst = part + (size_t)m * a.H;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = n0 + acc_col(wn, j, lane);
-          if (col < a.H) dst[col] = fmaf(-wr, bf16_bits_to_float(wrow[col]), acc.c[i][j][e]);
+          if (col < a.H) dst[col] = acc.c[i][j][e];
         }
       }
     }
@@ -365,15 +415,41 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_dh_gemm(DhArgs a) {
   }
 }
 
+// one block per completion position: dH = sum of partials - w W[target]
+__global__ __launch_bounds__(256) void k_dh_finish(DhFinishArgs a) {
+  const int m = blockIdx.x;
+  if (m >= a.hdr->n_c) return;
+  const int tg = a.tgt_c[m];
+  const float wr = tg >= 0 ? a.weight[a.row_c[m]] : 0.f;
+  const uint16_t* wrow = a.w + (size_t)(tg >= 0 ? tg : 0) * a.H;
+  float* dst = a.d_hidden + (size_t)a.idx[m] * a.H;
+  for (int c = threadIdx.x * 4; c < a.H; c += 256 * 4) {
+    float4 s = *(const float4*)(a.part + (size_t)m * a.H + c);
+    for (int ks = 1; ks < a.splitk; ++ks) {
+      const float4 p = *(const float4*)(a.part + ((size_t)ks * a.Mp + m) * a.H + c);
+      s.x += p.x;
+      s.y += p.y;
+      s.z += p.z;
+      s.w += p.w;
+    }
+    const uint2 wv = *(const uint2*)(wrow + c);
+    s.x = fmaf(-wr, bf16_lo(wv.x), s.x);
+    s.y = fmaf(-wr, bf16_hi(wv.x), s.y);
+    s.z = fmaf(-wr, bf16_lo(wv.y), s.z);
+    s.w = fmaf(-wr, bf16_hi(wv.y), s.w);
+    *(float4*)(dst + c) = s;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dW_vocab = D^T . Hc  (A = D^T rows, B = Hc^T rows), K = completion positions
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NTHREADS, 1) void k_dw_gemm(DwArgs a) {
+__global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int n_c = a.hdr->n_c;
   const int nk = cdiv(n_c, BK);
   Sched sc;
@@ -392,7 +468,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_dw_gemm(DwArgs a) {
       brows[it] = a.ht + (size_t)min(n0 + r, a.H - 1) * a.Mp + lchunk * 8;
     }
     Acc acc;
-    mainloop(acc, arows, brows, nk, smem, wave, lane, wm, wn);
+    mainloop<false>(acc, arows, brows, 0, nk, smem, wave, lane, wm, wn);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -579,6 +655,11 @@ hipError_t launch_dprod_gemm(const DProdArgs& a, int grid, hipStream_t s) {
   static hipError_t once = prep_gemm((const void*)k_dprod_gemm);
   if (once != hipSuccess) return once;
   hipLaunchKernelGGL(k_dprod_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dh_finish(const DhFinishArgs& a, int Mp, hipStream_t s) {
+  hipLaunchKernelGGL(k_dh_finish, dim3(Mp), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

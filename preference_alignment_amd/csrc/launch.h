@@ -86,13 +86,20 @@ struct DProdArgs {
 struct DhArgs {
   const uint16_t* D;
   const uint16_t* wt;
+  int H, Vp, Mp, gm, splitk;
+  const WsHeader* hdr;
+  float* part;  // [splitk, Mp, H] fp32 partial sums
+};
+
+struct DhFinishArgs {
+  const float* part;
   const uint16_t* w;    // [V, H] for the exact one-hot term
-  int H, Vp, Mp, gm;
   const int* idx;
   const int* tgt_c;
   const int* row_c;
   const float* weight;  // [rows]
   const WsHeader* hdr;
+  int H, Mp, splitk;
   float* d_hidden;  // [rows*T, H]
 };
 
@@ -175,6 +182,7 @@ hipError_t launch_transpose_w(const TransposeWArgs& a, hipStream_t s);
 hipError_t launch_gather_ht(const GatherHTArgs& a, hipStream_t s);
 hipError_t launch_dprod_gemm(const DProdArgs& a, int grid, hipStream_t s);
 hipError_t launch_dh_gemm(const DhArgs& a, int grid, hipStream_t s);
+hipError_t launch_dh_finish(const DhFinishArgs& a, int Mp, hipStream_t s);
 hipError_t launch_dw_gemm(const DwArgs& a, int grid, hipStream_t s);
 hipError_t launch_zero_rows(const ZeroRowsArgs& a, long positions, hipStream_t s);
 hipError_t launch_sort_targets(const SortArgs& a, hipStream_t s);
