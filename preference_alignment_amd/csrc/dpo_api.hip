@@ -35,7 +35,7 @@ struct Layout {
   size_t hdr = 0, idx = 0, tgt = 0, rowc = 0, rowoff = 0;
   size_t part = 0, tlogit = 0, lse64 = 0, logp64 = 0;
   size_t D = 0, DT = 0, WT = 0, HT = 0;
-  size_t keysA = 0, valsA = 0, keysB = 0, valsB = 0, counters = 0, dhpart = 0;
+  size_t keysA = 0, valsA = 0, keysB = 0, valsB = 0, counters = 0, dhpart = 0, spos = 0, sw = 0, ohcont = 0, ohhead = 0;
   size_t total = 0;
 };
 
@@ -88,6 +88,10 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     L.valsB = take((size_t)L.Mp * 4);
     L.counters = take((size_t)kSortThreads * 256 * 4);
     L.dhpart = take((size_t)kSplitDh * L.Mp * H * 4);
+    L.spos = take((size_t)L.Mp * 4);
+    L.sw = take((size_t)L.Mp * 4);
+    L.ohcont = take((size_t)(L.Mp / 64) * H * 4);
+    L.ohhead = take((size_t)(L.Mp / 64) * H * 4);
   }
   L.total = o;
   return L;
@@ -420,6 +424,9 @@ int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int
   while (bits < 31 && (1 << bits) < V) ++bits;
   SortArgs so;
   so.tgt_c = dp.tgt_c;
+  so.idx = dp.idx;
+  so.row_c = dp.row_c;
+  so.weight = weight;
   so.hdr = hdr;
   so.passes = (bits + 7) / 8;
   so.keysA = at<int>(ws, L.keysA);
@@ -427,17 +434,19 @@ int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int
   so.keysB = at<int>(ws, L.keysB);
   so.valsB = at<int>(ws, L.valsB);
   so.counters = at<int>(ws, L.counters);
+  so.s_pos = at<int>(ws, L.spos);
+  so.s_w = at<float>(ws, L.sw);
   RUN("sort_targets", launch_sort_targets(so, st));
   OnehotDwArgs oh;
   oh.keys = (so.passes & 1) ? so.keysB : so.keysA;
-  oh.vals = (so.passes & 1) ? so.valsB : so.valsA;
-  oh.idx = dp.idx;
-  oh.row_c = dp.row_c;
-  oh.weight = weight;
+  oh.s_pos = so.s_pos;
+  oh.s_w = so.s_w;
   oh.hidden = hidden;
   oh.hdr = hdr;
   oh.H = H;
   oh.V = V;
+  oh.cont = at<float>(ws, L.ohcont);
+  oh.head = at<float>(ws, L.ohhead);
   oh.d_w = d_w_vocab;
   RUN("onehot_dw", launch_onehot_dw(oh, L.Mp, st));
   return DPO_OK;

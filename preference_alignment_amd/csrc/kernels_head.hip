@@ -15,7 +15,7 @@
 //   k_compact        completion positions (row-major), per-row offsets, targets check
 //   k_fwd_gemm       Z tile = Hc . W^T on MFMA; epilogue: per-row (max, sum exp) over
 //                    the tile's columns and capture of the target logit
-//   k_combine        fp64 combine of the per-tile (max, sum exp) -> lse, log p
+//   k_combine        combine of the per-tile (max, sum exp), fp64 sums -> lse, log p
 //   k_row_sums       fp64 per-row sums in a fixed order
 //   k_transpose_w    W^T (bf16) for the dHidden contraction
 //   k_gather_ht      Hc^T (bf16) for the dW contraction
@@ -24,7 +24,7 @@
 //   k_dh_finish      dHidden rows = sum of partials - w W[target], scattered to their positions
 //   k_dw_gemm        dW_vocab = D^T . Hc (overwrite or accumulate)
 //   k_sort_targets   completion positions stably sorted by target id
-//   k_onehot_dw      dW_vocab[y] -= sum of w h over the positions whose target is y
+//   k_onehot_dw(+_join) dW_vocab[y] -= sum of w h over the positions whose target is y
 //
 // The one-hot term of dlogits is kept out of the bf16 operand D: rounding the
 // single large entry w (p_y - 1) to bf16 alone would cost ~1e-3 relative error
@@ -186,24 +186,52 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// combine per-tile partials: lse = M + log(sum_j s_j exp(m_j - M)), in fp64
+// combine per-tile partials: lse = M + log(sum_j s_j exp(m_j - M))
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
-  const int m = blockIdx.x * 256 + threadIdx.x;
+// A block takes 16 positions; its 16 thread groups split the vocabulary tiles
+// (tile j goes to group j % 16).  The global max comes first, then each group
+// accumulates its share of sum_j s_j exp(m_j - M) in fp64 and the 16 shares
+// are added in group order, so the result does not depend on timing.
+constexpr int kCombPos = 16;
+constexpr int kCombGroups = 16;
+
+__global__ __launch_bounds__(kCombPos * kCombGroups) void k_combine(CombineArgs a) {
+  __shared__ float red_m[kCombGroups][kCombPos];
+  __shared__ double red_s[kCombGroups][kCombPos];
+  const int p = threadIdx.x % kCombPos, g = threadIdx.x / kCombPos;
+  const int m = blockIdx.x * kCombPos + p;
   const int n_c = a.hdr->n_c;
-  if (m >= n_c) return;
+  if (blockIdx.x * kCombPos >= n_c) return;
+  const bool live = m < n_c;
   float M = -INFINITY;
-  for (int j = 0; j < a.nVt; ++j) M = fmaxf(M, a.part[(size_t)j * a.Mp + m].x);
-  double S = 0.0;
-  for (int j = 0; j < a.nVt; ++j) {
-    const float2 p = a.part[(size_t)j * a.Mp + m];
-    S += (double)p.y * exp((double)p.x - (double)M);
+  if (live) {
+#pragma unroll 4
+    for (int j = g; j < a.nVt; j += kCombGroups) M = fmaxf(M, a.part[(size_t)j * a.Mp + m].x);
   }
-  const double lse = (double)M + log(S);
-  const int t = a.tgt_c[m];
-  a.lse64[m] = lse;
-  a.logp64[m] = t >= 0 ? (double)a.tgt_logit[m] - lse : __builtin_nan("");
-  if (a.lse_out) a.lse_out[a.idx[m]] = (float)lse;
+  red_m[g][p] = M;
+  __syncthreads();
+  M = red_m[0][p];
+  for (int q = 1; q < kCombGroups; ++q) M = fmaxf(M, red_m[q][p]);
+  double S = 0.0;
+  if (live) {
+    const float Ml = M * kLog2e;
+#pragma unroll 4
+    for (int j = g; j < a.nVt; j += kCombGroups) {
+      const float2 t = a.part[(size_t)j * a.Mp + m];
+      S += (double)(t.y * fast_exp2(fmaf(t.x, kLog2e, -Ml)));
+    }
+  }
+  red_s[g][p] = S;
+  __syncthreads();
+  if (g == 0 && live) {
+    S = red_s[0][p];
+    for (int q = 1; q < kCombGroups; ++q) S += red_s[q][p];
+    const double lse = (double)M + log(S);
+    const int t = a.tgt_c[m];
+    a.lse64[m] = lse;
+    a.logp64[m] = t >= 0 ? (double)a.tgt_logit[m] - lse : __builtin_nan("");
+    if (a.lse_out) a.lse_out[a.idx[m]] = (float)lse;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -233,17 +261,33 @@ __global__ __launch_bounds__(256) void k_row_sums(RowSumArgs a) {
 // ---------------------------------------------------------------------------
 // operand transposes for the backward contractions
 // ---------------------------------------------------------------------------
-// W [V, H] -> WT [H, Vp], zero columns v >= V.  64x64 tiles through LDS.
+// W [V, H] -> WT [H, Vp], zero columns v >= V.  64x64 tiles through LDS,
+// 16-byte global reads and writes.
 __global__ __launch_bounds__(256) void k_transpose_w(TransposeWArgs a) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ uint16_t tile[64][72];
   const int v0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = it * 256 + tid;        // 64 rows x 8 chunks
+    const int r = q >> 3, c = q & 7;
     const int v = v0 + r;
-    tile[r][tx] = v < a.V ? a.w[(size_t)v * a.H + h0 + tx] : (uint16_t)0;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (v < a.V) val = *(const u32x4*)(a.w + (size_t)v * a.H + h0 + c * 8);
+    *(u32x4*)&tile[r][c * 8] = val;
   }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) a.wt[(size_t)(h0 + r) * a.Vp + v0 + tx] = tile[tx][r];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = it * 256 + tid;        // 64 output rows (h) x 8 chunks of 8 v
+    const int h = q >> 3, c = q & 7;
+    uint32_t w4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w4[u] = (uint32_t)tile[c * 8 + 2 * u][h] | ((uint32_t)tile[c * 8 + 2 * u + 1][h] << 16);
+    const u32x4 o = {w4[0], w4[1], w4[2], w4[3]};
+    *(u32x4*)(a.wt + (size_t)(h0 + h) * a.Vp + v0 + c * 8) = o;
+  }
 }
 
 // hidden rows at completion positions -> HT [H, Mp], zero columns m >= n_c.
@@ -543,63 +587,113 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_targets(SortArgs a) {
     kout = (kout == a.keysB) ? a.keysA : a.keysB;
     vout = (vout == a.valsB) ? a.valsA : a.valsB;
   }
+  // per sorted entry: flat position and row weight, read by k_onehot_dw
+  for (int i = lo; i < hi; ++i) {
+    const int m = vin[i];
+    a.s_pos[i] = a.idx[m];
+    a.s_w[i] = a.weight[a.row_c[m]];
+  }
 }
 
-// Each block takes 64 consecutive entries of the sorted list and, for every
-// run of equal targets that starts there, subtracts sum_t w_t h_t (ascending t)
-// from that dW_vocab row, 1024 columns per block (4 per thread).
+// Two phases over the sorted list, cut in chunks of 64 entries (1024 columns
+// per block, 4 per thread).  Phase 1 sums, in ascending position order, every
+// piece of a run of equal targets that lies in its chunk: a run contained in
+// the chunk is subtracted from its dW_vocab row at once; the piece of a run
+// that started in an earlier chunk goes to cont[chunk], the piece of a run
+// that continues into the next chunk goes to head[chunk].  Phase 2 adds, for
+// each run that crosses chunks, head and the following cont pieces in chunk
+// order and subtracts the total.  The order of every sum is fixed.
 constexpr int kOnehotChunk = 64;
 constexpr int kOnehotCols = 1024;
+constexpr int kOnehotUnroll = 16;
+
+__device__ __forceinline__ float4 onehot_piece(const OnehotDwArgs& a, int j, int e, int c0) {
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  for (; j + kOnehotUnroll <= e; j += kOnehotUnroll) {
+    uint2 hh[kOnehotUnroll];
+#pragma unroll
+    for (int u = 0; u < kOnehotUnroll; ++u) hh[u] = *(const uint2*)(a.hidden + (size_t)a.s_pos[j + u] * a.H + c0);
+#pragma unroll
+    for (int u = 0; u < kOnehotUnroll; ++u) {
+      const float w = a.s_w[j + u];
+      acc0 = fmaf(w, bf16_lo(hh[u].x), acc0);
+      acc1 = fmaf(w, bf16_hi(hh[u].x), acc1);
+      acc2 = fmaf(w, bf16_lo(hh[u].y), acc2);
+      acc3 = fmaf(w, bf16_hi(hh[u].y), acc3);
+    }
+  }
+  for (; j < e; ++j) {
+    const uint2 h = *(const uint2*)(a.hidden + (size_t)a.s_pos[j] * a.H + c0);
+    const float w = a.s_w[j];
+    acc0 = fmaf(w, bf16_lo(h.x), acc0);
+    acc1 = fmaf(w, bf16_hi(h.x), acc1);
+    acc2 = fmaf(w, bf16_lo(h.y), acc2);
+    acc3 = fmaf(w, bf16_hi(h.y), acc3);
+  }
+  return make_float4(acc0, acc1, acc2, acc3);
+}
+
+__device__ __forceinline__ void sub4(float* dst, float4 v) {
+  float4 d = *(float4*)dst;
+  d.x -= v.x;
+  d.y -= v.y;
+  d.z -= v.z;
+  d.w -= v.w;
+  *(float4*)dst = d;
+}
 
 __global__ __launch_bounds__(256) void k_onehot_dw(OnehotDwArgs a) {
   const int n = a.hdr->n_c;
-  const int i0 = blockIdx.x * kOnehotChunk;
+  const int ch = blockIdx.x;
+  const int i0 = ch * kOnehotChunk;
   const int c0 = blockIdx.y * kOnehotCols + threadIdx.x * 4;
   if (i0 >= n || c0 >= a.H) return;
   const int i1 = min(n, i0 + kOnehotChunk);
-  for (int i = i0; i < i1; ++i) {
+  int i = i0;
+  while (i < i1) {
     const int k = a.keys[i];
-    if ((i > 0 && a.keys[i - 1] == k) || k < 0 || k >= a.V) continue;
     int e = i + 1;
-    while (e < n && a.keys[e] == k) ++e;
-    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-    int j = i;
-    for (; j + 4 <= e; j += 4) {
-      int mm[4];
-      float ww[4];
-      uint2 hh[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) mm[u] = a.vals[j + u];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        ww[u] = a.weight[a.row_c[mm[u]]];
-        hh[u] = *(const uint2*)(a.hidden + (size_t)a.idx[mm[u]] * a.H + c0);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc0 = fmaf(ww[u], bf16_lo(hh[u].x), acc0);
-        acc1 = fmaf(ww[u], bf16_hi(hh[u].x), acc1);
-        acc2 = fmaf(ww[u], bf16_lo(hh[u].y), acc2);
-        acc3 = fmaf(ww[u], bf16_hi(hh[u].y), acc3);
-      }
+    while (e < i1 && a.keys[e] == k) ++e;
+    const bool starts_here = i > 0 ? a.keys[i - 1] != k : true;
+    const bool ends_here = e < i1 || i1 == n || a.keys[i1] != k;
+    if (k >= 0 && k < a.V) {
+      const float4 v = onehot_piece(a, i, e, c0);
+      if (!starts_here)
+        *(float4*)(a.cont + (size_t)ch * a.H + c0) = v;
+      else if (!ends_here)
+        *(float4*)(a.head + (size_t)ch * a.H + c0) = v;
+      else
+        sub4(a.d_w + (size_t)k * a.H + c0, v);
     }
-    for (; j < e; ++j) {
-      const int m = a.vals[j];
-      const float w = a.weight[a.row_c[m]];
-      const uint2 h = *(const uint2*)(a.hidden + (size_t)a.idx[m] * a.H + c0);
-      acc0 = fmaf(w, bf16_lo(h.x), acc0);
-      acc1 = fmaf(w, bf16_hi(h.x), acc1);
-      acc2 = fmaf(w, bf16_lo(h.y), acc2);
-      acc3 = fmaf(w, bf16_hi(h.y), acc3);
-    }
-    float4* dst = (float4*)(a.d_w + (size_t)k * a.H + c0);
-    float4 v = *dst;
-    v.x -= acc0;
-    v.y -= acc1;
-    v.z -= acc2;
-    v.w -= acc3;
-    *dst = v;
+    i = e;
   }
+}
+
+__global__ __launch_bounds__(256) void k_onehot_dw_join(OnehotDwArgs a) {
+  const int n = a.hdr->n_c;
+  const int ch = blockIdx.x;
+  const int i0 = ch * kOnehotChunk;
+  const int c0 = blockIdx.y * kOnehotCols + threadIdx.x * 4;
+  if (i0 >= n || c0 >= a.H) return;
+  const int i1 = min(n, i0 + kOnehotChunk);
+  if (i1 == n) return;
+  const int k = a.keys[i1 - 1];
+  if (a.keys[i1] != k || k < 0 || k >= a.V) return;  // the last run does not cross into the next chunk
+  // the last run must also start in this chunk (otherwise an earlier chunk owns it)
+  int s0 = i1 - 1;
+  while (s0 > i0 && a.keys[s0 - 1] == k) --s0;
+  if (s0 == i0 && i0 > 0 && a.keys[i0 - 1] == k) return;
+  float4 t = *(const float4*)(a.head + (size_t)ch * a.H + c0);
+  for (int c = ch + 1; c * kOnehotChunk < n; ++c) {
+    const float4 p = *(const float4*)(a.cont + (size_t)c * a.H + c0);
+    t.x += p.x;
+    t.y += p.y;
+    t.z += p.z;
+    t.w += p.w;
+    const int e = min(n, (c + 1) * kOnehotChunk);
+    if (e == n || a.keys[e] != k) break;  // the run ends in chunk c
+  }
+  sub4(a.d_w + (size_t)k * a.H + c0, t);
 }
 
 // dHidden rows outside the completion mask are exactly zero.
@@ -632,7 +726,7 @@ hipError_t launch_fwd_gemm(const FwdArgs& a, int grid, hipStream_t s) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3(a.Mp / 256), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_combine, dim3(a.Mp / kCombPos), dim3(kCombPos * kCombGroups), 0, s, a);
   return hipGetLastError();
 }
 
@@ -683,7 +777,11 @@ hipError_t launch_sort_targets(const SortArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_onehot_dw(const OnehotDwArgs& a, int Mp, hipStream_t s) {
-  hipLaunchKernelGGL(k_onehot_dw, dim3(Mp / kOnehotChunk, cdiv(a.H, kOnehotCols)), dim3(256), 0, s, a);
+  const dim3 grid(Mp / kOnehotChunk, cdiv(a.H, kOnehotCols));
+  hipLaunchKernelGGL(k_onehot_dw, grid, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_onehot_dw_join, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

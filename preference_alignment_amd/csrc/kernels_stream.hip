@@ -87,6 +87,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_fwd(StreamFwdArgs a) 
   }
 }
 
+constexpr int kBwdUnroll = 8;
+
 __global__ __launch_bounds__(kStreamThreads) void k_stream_bwd(StreamBwdArgs a) {
   const size_t p = blockIdx.x;
   const int tid = threadIdx.x;
@@ -104,26 +106,32 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_bwd(StreamBwdArgs a) 
   }
   const float L = a.lse[p] * kLog2e;
   const float w = a.weight[p / a.T];
+  const int tv = tg >= 0 ? tg >> 3 : -1;  // the one vector holding the target
   const u32x4* row = (const u32x4*)(a.logits + p * a.V);
-  for (int v0 = tid; v0 < nvec; v0 += kStreamUnroll * kStreamThreads) {
-    u32x4 buf[kStreamUnroll];
+  for (int v0 = tid; v0 < nvec; v0 += kBwdUnroll * kStreamThreads) {
+    u32x4 buf[kBwdUnroll];
 #pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) {
+    for (int u = 0; u < kBwdUnroll; ++u) {
       const int v = v0 + u * kStreamThreads;
       if (v < nvec) buf[u] = __builtin_nontemporal_load(row + v);
     }
 #pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) {
+    for (int u = 0; u < kBwdUnroll; ++u) {
       const int v = v0 + u * kStreamThreads;
       if (v >= nvec) break;
-      u32x4 o;
+      float d[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int c = v * 8 + 2 * k;
-        float d0 = w * (fast_exp2(fmaf(bf16_lo(buf[u][k]), kLog2e, -L)) - (c == tg ? 1.f : 0.f));
-        float d1 = w * (fast_exp2(fmaf(bf16_hi(buf[u][k]), kLog2e, -L)) - (c + 1 == tg ? 1.f : 0.f));
-        o[k] = pack_bf16x2(d0, d1);
+        d[2 * k] = w * fast_exp2(fmaf(bf16_lo(buf[u][k]), kLog2e, -L));
+        d[2 * k + 1] = w * fast_exp2(fmaf(bf16_hi(buf[u][k]), kLog2e, -L));
       }
+      if (v == tv) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d[k] = (k == (tg & 7)) ? d[k] - w : d[k];
+      }
+      u32x4 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(d[2 * k], d[2 * k + 1]);
       __builtin_nontemporal_store(o, out + v);
     }
   }

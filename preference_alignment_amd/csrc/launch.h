@@ -105,6 +105,9 @@ struct DhFinishArgs {
 
 struct SortArgs {
   const int* tgt_c;     // [n_c] keys in position order
+  const int* idx;
+  const int* row_c;
+  const float* weight;  // [rows]
   const WsHeader* hdr;
   int passes;           // 8-bit digits needed to cover V
   int* keysA;
@@ -112,17 +115,19 @@ struct SortArgs {
   int* keysB;
   int* valsB;
   int* counters;        // [kSortThreads * 256]
+  int* s_pos;           // [n_c] flat position of each sorted entry
+  float* s_w;           // [n_c] its row weight
 };
 
 struct OnehotDwArgs {
   const int* keys;      // [n_c] targets, sorted
-  const int* vals;      // [n_c] compact positions, ascending within a target
-  const int* idx;
-  const int* row_c;
-  const float* weight;
+  const int* s_pos;     // [n_c] flat positions, ascending within a target
+  const float* s_w;     // [n_c] row weights
   const uint16_t* hidden;
   const WsHeader* hdr;
   int H, V;
+  float* cont;  // [Mp/64, H] piece of a run that started in an earlier chunk
+  float* head;  // [Mp/64, H] piece of a run that continues into the next chunk
   float* d_w;
 };
 
