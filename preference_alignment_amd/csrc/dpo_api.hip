@@ -382,6 +382,7 @@ int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int
   dh.D = D;
   dh.wt = WT;
   dh.H = H;
+  dh.V = V;
   dh.Vp = L.Vp;
   dh.Mp = L.Mp;
   dh.gm = kGroupBwd;

@@ -1,11 +1,11 @@
 // bf16 MFMA main loop shared by the four LM-head contractions (gfx950).
 //
-// C[i][j] = sum_k A[i][k] * B[j][k]: both operands K-contiguous ("NT").  The
-// kernels that use this core differ only in where operand rows come from and
-// in their epilogues:
-//   forward / recompute : A = hidden rows at completion positions, B = W_vocab
-//   dHidden             : A = D (dlogits, bf16), B = W_vocab^T
-//   dW_vocab            : A = D^T,              B = hidden^T at completion positions
+// C[i][j] = sum_k R[i][k] * C[k][j] with each operand either K-contiguous
+// (ROW layout) or contiguous along its MFMA dimension (TR layout).  The
+// kernels that use this core differ in their operands and epilogues:
+//   forward / recompute : R = W_vocab rows (ROW), C = hidden rows at completion positions (ROW)
+//   dHidden             : R = D rows (ROW),       C = W_vocab (TR: K = vocabulary rows)
+//   dW_vocab            : R = D (TR: K = positions), C = gathered hidden (TR)
 //
 // Block tile 256x256x64, 512 threads = 8 waves in a 2x4 grid (two waves per
 // SIMD, so one wave's LDS and barrier waits are covered by the other's MFMAs);
@@ -18,12 +18,8 @@
 // current one issue, and the stage barrier sits inside the MFMA stream of the
 // last step of a stage, with the next stage's first fragments read across it.
 //
-// LDS layout of one operand tile: 256 rows x 128 bytes (64 bf16 of K).  The
-// 16-byte chunk c of row r is stored at chunk position c ^ ((r >> 1) & 7) so
-// that the fragment reads (32 rows, same logical chunk) spread over all banks
-// (no bank conflicts measured).  global_load_lds places lane L's 16 bytes at
-// (wave base + 16 L), so the swizzle is realised by choosing which global
-// chunk each lane fetches.
+// global_load_lds places lane L's 16 bytes at (wave base + 16 L), so the LDS
+// swizzles below are realised by choosing which global chunk each lane fetches.
 //
 // MFMA 32x32x16 register layout (CDNA3/CDNA4 32x32 family): lane l supplies
 // A[l % 32][8 (l / 32) + 0..7] and B^T likewise; accumulator element e of lane
@@ -58,34 +54,109 @@ struct Acc {
   floatx16 c[FM][FN];
 };
 
-// Per-thread constants of the loader: this thread fetches rows
-// (it * 64 + tid / 8), it = 0..3, at logical chunk lchunk() of each K step.
-__device__ __forceinline__ int loader_row(int it, int tid) { return it * LOADER_ROW_STRIDE + (tid >> 3); }
-__device__ __forceinline__ int loader_lchunk(int tid) { return (tid & 7) ^ ((tid >> 4) & 7); }
+// Operand tiles come in two LDS layouts.
+//
+// ROW: the operand is K-contiguous in memory (rows of the MFMA dimension,
+// 64 K values each).  Tile = 256 rows x 128 bytes; the 16-byte chunk c of row
+// r sits at chunk c ^ ((r >> 1) & 7).  Fragments are single ds_read_b128.
+//
+// TR: the operand is contiguous along the MFMA dimension (rows = K).  Tile =
+// 64 K rows x 512 bytes (256 values); the 16-byte chunk c of K row r sits at
+// chunk c ^ 4 (r & 3), so the 4 rows x 2 chunks that each 16-lane group reads
+// land in distinct banks, and the two groups of a half-wave in disjoint ones.  Fragments come from two ds_read_b64_tr_b16 (gfx950
+// transposing LDS read): in each group of 16 lanes, lane L addresses K row
+// (L / 4) and columns 4 (L % 4) .. +3 of a 4 x 16 block, and lane i receives
+// the 4 K values of column i, which is the MFMA operand layout.
+struct RowOperand {
+  const uint16_t* rows[LOADS_PER_THREAD];  // element (row, lchunk * 8) at K = 0
+};
+struct TrOperand {
+  const uint16_t* base;  // element (K row 0, column 0) of the operand
+  size_t ld;             // elements between K rows
+  int col;               // this thread's column: tile column 0 + lchunk * 8 (clamped)
+  int row0;              // first K row of the loop
+  int rmax;              // last valid K row (rows beyond are clamped to it)
+  int kr0;               // this thread's first tile row
+};
 
-// Issue the global->LDS copies of one operand tile for one K step.
-// rows[it] points at element (row, lchunk*8) of the operand; k0 is the K offset.
-__device__ __forceinline__ void load_tile(const uint16_t* const (&rows)[LOADS_PER_THREAD], int k0,
-                                          char* lds_tile, int wave) {
+__device__ __forceinline__ int row_lchunk(int tid) { return (tid & 7) ^ ((tid >> 4) & 7); }
+__device__ __forceinline__ int row_loader_row(int it, int tid) { return it * LOADER_ROW_STRIDE + (tid >> 3); }
+__device__ __forceinline__ int tr_lchunk(int tid) { return (tid & 31) ^ (((tid >> 5) & 3) << 2); }
+__device__ __forceinline__ int tr_loader_row(int it, int tid) { return it * 16 + (tid >> 5); }
+
+__device__ __forceinline__ void load_stage(const RowOperand& op, int kstep, char* lds_tile, int wave) {
 #pragma unroll
   for (int it = 0; it < LOADS_PER_THREAD; ++it) {
     lds_ptr_t dst = (lds_ptr_t)(lds_tile + (it * NTHREADS + wave * 64) * 16);
-    __builtin_amdgcn_global_load_lds((const void*)(rows[it] + k0), dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(op.rows[it] + (size_t)kstep * BK), dst, 16, 0, 0);
+  }
+}
+__device__ __forceinline__ void load_stage(const TrOperand& op, int kstep, char* lds_tile, int wave) {
+#pragma unroll
+  for (int it = 0; it < LOADS_PER_THREAD; ++it) {
+    lds_ptr_t dst = (lds_ptr_t)(lds_tile + (it * NTHREADS + wave * 64) * 16);
+    const int r = min(op.row0 + kstep * BK + op.kr0 + it * 16, op.rmax);
+    __builtin_amdgcn_global_load_lds((const void*)(op.base + (size_t)r * op.ld + op.col), dst, 16, 0, 0);
   }
 }
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// The K loop over [k_begin, k_begin + nk*BK).  nk may be 0 (accumulators stay
-// zero).  The caller guarantees every row pointer is valid over that range.
-// SWAP = false: MFMA rows come from the first operand tile (arows) and
-// columns from the second (brows).  SWAP = true: the roles are exchanged, so
-// accumulator rows index the second operand and columns the first.
-// Wave (wm, wn) owns MFMA rows wm*128 .. +128 and columns wn*64 .. +64.
-template <bool SWAP>
-__device__ __forceinline__ void mainloop(Acc& acc, const uint16_t* const (&arows)[LOADS_PER_THREAD],
-                                         const uint16_t* const (&brows)[LOADS_PER_THREAD], int k_begin,
-                                         int nk, char* smem, int wave, int lane, int wm, int wn) {
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr;
+
+// Fragment readers.  `f` = fragment index along the MFMA dimension (32 wide),
+// `base` = first MFMA row/column of this wave inside the tile, kk = 16-wide K step.
+struct RowFrag {
+  int off[4];  // byte offset of (row, chunk of step kk) for fragment 0
+  __device__ __forceinline__ void init(int base, int lane) {
+    const int sw = (lane >> 1) & 7;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) off[kk] = (base + (lane & 31)) * 128 + (((2 * kk + (lane >> 5)) ^ sw) << 4);
+  }
+  __device__ __forceinline__ bf16x8_t read(const char* tile, int f, int kk) const {
+    return *(const bf16x8_t*)(tile + off[kk] + f * 4096);
+  }
+};
+template <int NF>
+struct TrFrag {
+  // byte offset of the two 4-row reads (h = 0, 1) of fragment f at K step 0;
+  // K step kk adds kk * 16 rows = kk * 8192 bytes (the swizzle depends only on
+  // the K row modulo 4, which a step of 16 rows leaves unchanged)
+  int off[NF][2];
+  __device__ __forceinline__ void init(int base, int lane) {
+    const int q = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int col = base + 32 * f + 16 * (q & 1) + 4 * (i & 3);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kr = 8 * (q >> 1) + (i >> 2) + 4 * h;
+        off[f][h] = kr * 512 + (((col >> 3) ^ ((kr & 3) << 2)) << 4) + ((col & 7) << 1);
+      }
+    }
+  }
+  __device__ __forceinline__ bf16x8_t read(const char* tile, int f, int kk) const {
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tile + off[f][0] + kk * 8192));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tile + off[f][1] + kk * 8192));
+    const short __attribute__((ext_vector_type(8))) v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+};
+
+template <typename Op, int NF> struct FragOf;
+template <int NF> struct FragOf<RowOperand, NF> { typedef RowFrag type; };
+template <int NF> struct FragOf<TrOperand, NF> { typedef TrFrag<NF> type; };
+
+// The K loop over nk steps of BK.  nk may be 0 (accumulators stay zero).  The
+// R operand supplies the MFMA rows (wave (wm, wn) owns rows wm*128 .. +128),
+// the C operand the MFMA columns (columns wn*64 .. +64).  Software pipelined:
+// the fragments of the next 16-wide K step are read while the MFMAs of the
+// current one issue, and the stage barrier sits inside the MFMA stream of the
+// last step of a stage, with the next stage's first fragments read across it.
+template <typename ROp, typename COp>
+__device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& cop, int nk, char* smem, int wave,
+                                         int lane, int wm, int wn) {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -94,31 +165,26 @@ __device__ __forceinline__ void mainloop(Acc& acc, const uint16_t* const (&arows
       for (int e = 0; e < 16; ++e) acc.c[i][j][e] = 0.f;
   if (nk <= 0) return;
 
-  // fragment read offsets (bytes) inside an operand tile
-  const int sw = (lane >> 1) & 7;
-  const int r_off = (wm * 128 + (lane & 31)) * 128 + (SWAP ? OPER_BYTES : 0);       // MFMA-row fragments
-  const int c_off = (wn * WAVE_COLS + (lane & 31)) * 128 + (SWAP ? 0 : OPER_BYTES);  // MFMA-column fragments
-  int choff[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) choff[kk] = (((2 * kk + (lane >> 5)) ^ sw) << 4);
-
+  typename FragOf<ROp, FM>::type rf;
+  typename FragOf<COp, FN>::type cf;
+  rf.init(wm * 128, lane);
+  cf.init(wn * WAVE_COLS, lane);
   bf16x8_t fa[2][FM], fb[2][FN];
 #define DPO_READ_FRAGS(stage_, kk_, slot_)                                                     \
   do {                                                                                         \
     const char* base_ = smem + (stage_) * STAGE_BYTES;                                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < FM; ++i_) fa[slot_][i_] =                          \
-        *(const bf16x8_t*)(base_ + r_off + i_ * 4096 + choff[kk_]);                            \
+    _Pragma("unroll") for (int i_ = 0; i_ < FM; ++i_) fa[slot_][i_] = rf.read(base_, i_, kk_); \
     _Pragma("unroll") for (int j_ = 0; j_ < FN; ++j_) fb[slot_][j_] =                          \
-        *(const bf16x8_t*)(base_ + c_off + j_ * 4096 + choff[kk_]);                            \
+        cf.read(base_ + OPER_BYTES, j_, kk_);                                                  \
   } while (0)
 
-  load_tile(arows, k_begin, smem, wave);
-  load_tile(brows, k_begin, smem + OPER_BYTES, wave);
+  load_stage(rop, 0, smem, wave);
+  load_stage(cop, 0, smem + OPER_BYTES, wave);
   wait_loads();
   __syncthreads();
   if (nk > 1) {
-    load_tile(arows, k_begin + BK, smem + STAGE_BYTES, wave);
-    load_tile(brows, k_begin + BK, smem + STAGE_BYTES + OPER_BYTES, wave);
+    load_stage(rop, 1, smem + STAGE_BYTES, wave);
+    load_stage(cop, 1, smem + STAGE_BYTES + OPER_BYTES, wave);
   }
   DPO_READ_FRAGS(0, 0, 0);
 
@@ -152,8 +218,8 @@ __device__ __forceinline__ void mainloop(Acc& acc, const uint16_t* const (&arows
           asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
           __builtin_amdgcn_s_barrier();
           if (kt + 2 < nk) {
-            load_tile(arows, k_begin + (kt + 2) * BK, smem + cur * STAGE_BYTES, wave);
-            load_tile(brows, k_begin + (kt + 2) * BK, smem + cur * STAGE_BYTES + OPER_BYTES, wave);
+            load_stage(rop, kt + 2, smem + cur * STAGE_BYTES, wave);
+            load_stage(cop, kt + 2, smem + cur * STAGE_BYTES + OPER_BYTES, wave);
           }
           DPO_READ_FRAGS(cur ^ 1, 0, 0);
         }

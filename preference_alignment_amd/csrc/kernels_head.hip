@@ -129,22 +129,21 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
   const int n_c = a.hdr->n_c;
   Sched sc;
   sc.init(cdiv(n_c, BM), cdiv(a.V, BN), a.gm);
-  const int lchunk = loader_lchunk(tid);
+  const int lchunk = row_lchunk(tid);
   for (int t = sc.begin; t < sc.end; t += sc.step) {
     int mt, nt;
     sc.coords(t, mt, nt);
     const int m0 = mt * BM, n0 = nt * BN;
-    const uint16_t* arows[LOADS_PER_THREAD];
-    const uint16_t* brows[LOADS_PER_THREAD];
+    RowOperand wop, hop;
 #pragma unroll
     for (int it = 0; it < LOADS_PER_THREAD; ++it) {
-      const int r = loader_row(it, tid);
-      arows[it] = a.hidden + (size_t)a.idx[m0 + r] * a.H + lchunk * 8;
-      brows[it] = a.w + (size_t)min(n0 + r, a.V - 1) * a.H + lchunk * 8;
+      const int r = row_loader_row(it, tid);
+      wop.rows[it] = a.w + (size_t)min(n0 + r, a.V - 1) * a.H + lchunk * 8;
+      hop.rows[it] = a.hidden + (size_t)a.idx[m0 + r] * a.H + lchunk * 8;
     }
     if (tid < BM) tgt_s[tid] = a.tgt_c[m0 + tid];
     Acc acc;
-    mainloop<true>(acc, arows, brows, 0, a.H / BK, smem, wave, lane, wm, wn);
+    mainloop(acc, wop, hop, a.H / BK, smem, wave, lane, wm, wn);
 
     const int vbase = n0 + wm * 128;  // first vocabulary row of this wave
     const bool full = n0 + BN <= a.V;
@@ -308,14 +307,14 @@ __global__ __launch_bounds__(256) void k_gather_ht(GatherHTArgs a) {
 // ---------------------------------------------------------------------------
 // backward: recompute Z, D = w exp(z - lse) in bf16, written in both layouts
 // ---------------------------------------------------------------------------
-// Same exchanged-role MFMA as the forward: a lane holds 4 consecutive
-// vocabulary entries of one position per accumulator group, packed to one
-// 8-byte LDS write.  The bf16 tile (256 positions x 256 vocabulary, 128 KiB)
-// is staged in the freed pipeline LDS and leaves as 16-byte coalesced rows of
-// D [Mp, Vp] and of D^T [Vp, Mp].  Staging layout: 16-byte chunk c of
-// position row p sits at chunk c ^ f(p), f(p) = (p ^ (p >> 3)) & 31, which
-// keeps both the row-wise writes/reads and the column-wise (transposing)
-// reads free of bank conflicts.
+// Same MFMA orientation as the forward (rows = vocabulary, columns =
+// positions): a lane holds 4 consecutive vocabulary entries of one position
+// per accumulator group, packed to one 8-byte LDS write.  The bf16 tile (256
+// positions x 256 vocabulary, 128 KiB) is staged in the freed pipeline LDS
+// and leaves as 16-byte coalesced rows of D [Mp, Vp] and of D^T [Vp, Mp].
+// Staging layout: the 16-byte chunk c of position row p sits at chunk
+// c ^ f(p), f(p) = (p ^ (p >> 3)) & 31, which keeps both the row-wise
+// writes/reads and the column-wise (transposing) reads free of bank conflicts.
 __device__ __forceinline__ int stage_off(int p, int v) {
   const int f = (p ^ (p >> 3)) & 31;
   return p * 512 + ((((v >> 3) ^ f)) << 4) + ((v & 7) << 1);
@@ -332,18 +331,17 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
   const int n_c = a.hdr->n_c;
   Sched sc;
   sc.init(cdiv(n_c, BM), a.Vp / BN, a.gm);
-  const int lchunk = loader_lchunk(tid);
+  const int lchunk = row_lchunk(tid);
   for (int t = sc.begin; t < sc.end; t += sc.step) {
     int mt, nt;
     sc.coords(t, mt, nt);
     const int m0 = mt * BM, n0 = nt * BN;
-    const uint16_t* arows[LOADS_PER_THREAD];
-    const uint16_t* brows[LOADS_PER_THREAD];
+    RowOperand wop, hop;
 #pragma unroll
     for (int it = 0; it < LOADS_PER_THREAD; ++it) {
-      const int r = loader_row(it, tid);
-      arows[it] = a.hidden + (size_t)a.idx[m0 + r] * a.H + lchunk * 8;
-      brows[it] = a.w + (size_t)min(n0 + r, a.V - 1) * a.H + lchunk * 8;
+      const int r = row_loader_row(it, tid);
+      wop.rows[it] = a.w + (size_t)min(n0 + r, a.V - 1) * a.H + lchunk * 8;
+      hop.rows[it] = a.hidden + (size_t)a.idx[m0 + r] * a.H + lchunk * 8;
     }
     if (tid < BM) {
       const int m = m0 + tid;
@@ -352,7 +350,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
       w_s[tid] = live ? a.weight[a.row_c[m]] : 0.f;
     }
     Acc acc;
-    mainloop<true>(acc, arows, brows, 0, a.H / BK, smem, wave, lane, wm, wn);
+    mainloop(acc, wop, hop, a.H / BK, smem, wave, lane, wm, wn);
 
     // D values (bf16) into the staging tile; the pipeline LDS is free now
 #pragma unroll
@@ -406,7 +404,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dHidden = D . W  (A = D rows, B = W^T rows), K = vocabulary split in `splitk`
+// dHidden = D . W  (R = D rows, C = W^T rows), K = vocabulary split in `splitk`
 // parts written as fp32 partials; k_dh_finish adds them in a fixed order,
 // applies the exact one-hot term and scatters rows to their positions.
 // ---------------------------------------------------------------------------
@@ -422,24 +420,24 @@ __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
   const int nks = cdiv(nkt, a.splitk);
   Sched sc;
   sc.init(cdiv(n_c, BM), nNt * a.splitk, a.gm);
-  const int lchunk = loader_lchunk(tid);
+  const int lchunk = row_lchunk(tid);
   for (int t = sc.begin; t < sc.end; t += sc.step) {
     int mt, ntk;
     sc.coords(t, mt, ntk);
     const int nt = ntk % nNt, ks = ntk / nNt;
     const int m0 = mt * BM, n0 = nt * BN;
-    const uint16_t* arows[LOADS_PER_THREAD];
-    const uint16_t* brows[LOADS_PER_THREAD];
-#pragma unroll
-    for (int it = 0; it < LOADS_PER_THREAD; ++it) {
-      const int r = loader_row(it, tid);
-      arows[it] = a.D + (size_t)(m0 + r) * a.Vp + lchunk * 8;
-      brows[it] = a.wt + (size_t)min(n0 + r, a.H - 1) * a.Vp + lchunk * 8;
-    }
     const int kb = ks * nks;
     const int nk = max(0, min(nks, nkt - kb));
+    RowOperand dop;
+#pragma unroll
+    for (int it = 0; it < LOADS_PER_THREAD; ++it)
+      dop.rows[it] = a.D + (size_t)(m0 + row_loader_row(it, tid)) * a.Vp + (size_t)kb * BK + lchunk * 8;
+    RowOperand wop;
+#pragma unroll
+    for (int it = 0; it < LOADS_PER_THREAD; ++it)
+      wop.rows[it] = a.wt + (size_t)min(n0 + row_loader_row(it, tid), a.H - 1) * a.Vp + (size_t)kb * BK + lchunk * 8;
     Acc acc;
-    mainloop<false>(acc, arows, brows, kb * BK, nk, smem, wave, lane, wm, wn);
+    mainloop(acc, dop, wop, nk, smem, wave, lane, wm, wn);
     float* part = a.part + (size_t)ks * a.Mp * a.H;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -486,7 +484,7 @@ __global__ __launch_bounds__(256) void k_dh_finish(DhFinishArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dW_vocab = D^T . Hc  (A = D^T rows, B = Hc^T rows), K = completion positions
+// dW_vocab = D^T . Hc  (R = D^T rows, C = Hc^T rows), K = completion positions
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -498,21 +496,20 @@ __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
   const int nk = cdiv(n_c, BK);
   Sched sc;
   sc.init(a.Vp / BM, cdiv(a.H, BN), a.gm);
-  const int lchunk = loader_lchunk(tid);
+  const int lchunk = row_lchunk(tid);
   for (int t = sc.begin; t < sc.end; t += sc.step) {
     int mt, nt;
     sc.coords(t, mt, nt);
     const int m0 = mt * BM, n0 = nt * BN;
-    const uint16_t* arows[LOADS_PER_THREAD];
-    const uint16_t* brows[LOADS_PER_THREAD];
+    RowOperand dop, hop;
 #pragma unroll
     for (int it = 0; it < LOADS_PER_THREAD; ++it) {
-      const int r = loader_row(it, tid);
-      arows[it] = a.DT + (size_t)(m0 + r) * a.Mp + lchunk * 8;
-      brows[it] = a.ht + (size_t)min(n0 + r, a.H - 1) * a.Mp + lchunk * 8;
+      const int r = row_loader_row(it, tid);
+      dop.rows[it] = a.DT + (size_t)(m0 + r) * a.Mp + lchunk * 8;
+      hop.rows[it] = a.ht + (size_t)min(n0 + r, a.H - 1) * a.Mp + lchunk * 8;
     }
     Acc acc;
-    mainloop<false>(acc, arows, brows, 0, nk, smem, wave, lane, wm, wn);
+    mainloop(acc, dop, hop, nk, smem, wave, lane, wm, wn);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll

@@ -85,8 +85,8 @@ struct DProdArgs {
 
 struct DhArgs {
   const uint16_t* D;
-  const uint16_t* wt;
-  int H, Vp, Mp, gm, splitk;
+  const uint16_t* wt;   // [H, Vp]
+  int H, V, Vp, Mp, gm, splitk;
   const WsHeader* hdr;
   float* part;  // [splitk, Mp, H] fp32 partial sums
 };
@@ -132,8 +132,8 @@ struct OnehotDwArgs {
 };
 
 struct DwArgs {
-  const uint16_t* DT;
-  const uint16_t* ht;
+  const uint16_t* DT;   // [Vp, Mp]
+  const uint16_t* ht;   // [H, Mp]
   int V, H, Vp, Mp, gm, accumulate;
   const WsHeader* hdr;
   float* d_w;  // [V, H]

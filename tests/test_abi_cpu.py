@@ -37,7 +37,7 @@ def test_workspace_sizes(L):
     # logits ops ignore H
     assert D.dpo_workspace_bytes(D.DPO_OP_LOGITS_SEQ_LOGPS, 8, 2048, 0, 128256) > 0
     assert D.dpo_workspace_bytes(D.DPO_OP_LOGITS_BACKWARD, 8, 2048, 0, 128256) == 256
-    # the backward holds D and D^T in bf16: at least 2 * 2 * (rows*T) * V bytes
+    # the backward holds the bf16 softmax part of dlogits in both layouts: >= 2 * 2 * (rows*T) * V bytes
     bw = D.dpo_workspace_bytes(D.DPO_OP_HEAD_BACKWARD, 8, 2048, 4096, 128256)
     assert bw >= 4 * 8 * 2048 * 128256
     # more rows never need less
