@@ -30,8 +30,8 @@
  *    marks a completion position.  Targets at mask-0 positions are never
  *    read as indices (they may hold the ignore value -100).
  *  - Shape rules: rows even and > 0; T, H, V > 0; H % 64 == 0; V % 8 == 0;
- *    rows*T < 2^31.  Pointers to bf16 and float arrays must be 16-byte
- *    aligned.
+ *    rows*T < 2^31; the hidden tensor under 4 GiB (rows*T*H < 2^31).
+ *    Pointers to bf16 and float arrays must be 16-byte aligned.
  *  - Target ids outside [0, V) at completion positions are detected on the
  *    device: the call's outputs for that position are NaN and
  *    dpo_device_status() reports DPO_ERR_TARGET_RANGE.

@@ -44,6 +44,8 @@ bool shape_ok(int rows, int T, int H, int V, bool need_h) {
   if ((long long)rows * T >= (1LL << 31) - gemm::BM) return false;
   if (V >= (1 << 30)) return false;
   if (need_h && (H <= 0 || H % 64 || H >= (1 << 30))) return false;
+  // the hidden tensor is addressed with 32-bit byte offsets
+  if (need_h && (long long)rows * T * H * 2 >= (1LL << 32)) return false;
   return true;
 }
 
@@ -237,6 +239,7 @@ int enqueue_fused_forward(const dpo_bf16* hidden, const dpo_bf16* w, const int32
   FwdArgs f;
   f.hidden = hidden;
   f.w = w;
+  f.hidden_bytes = (unsigned)((size_t)rows * T * H * 2);
   f.H = H;
   f.V = V;
   f.Mp = L.Mp;
@@ -363,6 +366,7 @@ int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int
   DProdArgs dp;
   dp.hidden = hidden;
   dp.w = w_vocab;
+  dp.hidden_bytes = (unsigned)((size_t)rows * T * H * 2);
   dp.H = H;
   dp.V = V;
   dp.Vp = L.Vp;

@@ -67,9 +67,32 @@ struct Acc {
 // transposing LDS read): in each group of 16 lanes, lane L addresses K row
 // (L / 4) and columns 4 (L % 4) .. +3 of a 4 x 16 block, and lane i receives
 // the 4 K values of column i, which is the MFMA operand layout.
+// ROW operands are read with buffer_load_dwordx4 ... lds: one uniform buffer
+// descriptor, a 32-bit byte offset per lane and loaded row (fixed for the
+// tile), and the K step in the scalar offset.  Offsets at or beyond the
+// descriptor's size read as zero, which is how ragged tiles are padded.
 struct RowOperand {
-  const uint16_t* rows[LOADS_PER_THREAD];  // element (row, lchunk * 8) at K = 0
+  __amdgpu_buffer_rsrc_t rsrc;
+  unsigned voff[LOADS_PER_THREAD];  // byte offset of (row, lchunk * 8) at K = 0
 };
+
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit dwords
+
+// Operand whose tile rows are consecutive rows of a row-major matrix:
+// `base` = first row of the tile, `ld` = elements per row, `rows_left` = rows
+// that exist from `base` on, `k0` = first K element.
+__device__ __forceinline__ RowOperand row_operand(const uint16_t* base, size_t ld, long rows_left, int k0,
+                                                  int tid) {
+  RowOperand op;
+  const size_t bytes = (size_t)max(rows_left, 0L) * ld * 2;
+  op.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
+                                              (int)min(bytes, (size_t)0xFFFFFFFFu), kBufferFlags);
+  const int lchunk = (tid & 7) ^ ((tid >> 4) & 7);
+#pragma unroll
+  for (int it = 0; it < LOADS_PER_THREAD; ++it)
+    op.voff[it] = (unsigned)(((size_t)(it * LOADER_ROW_STRIDE + (tid >> 3)) * ld + k0 + lchunk * 8) * 2);
+  return op;
+}
 struct TrOperand {
   const uint16_t* base;  // element (K row 0, column 0) of the operand
   size_t ld;             // elements between K rows
@@ -84,11 +107,27 @@ __device__ __forceinline__ int row_loader_row(int it, int tid) { return it * LOA
 __device__ __forceinline__ int tr_lchunk(int tid) { return (tid & 31) ^ (((tid >> 5) & 3) << 2); }
 __device__ __forceinline__ int tr_loader_row(int it, int tid) { return it * 16 + (tid >> 5); }
 
-__device__ __forceinline__ void load_stage(const RowOperand& op, int kstep, char* lds_tile, int wave) {
+// ROW operand read with global_load_lds from per-row 64-bit pointers.  Same
+// LDS layout as RowOperand; measured faster than buffer loads for the
+// dHidden contraction, whose two operands both stride 256 KiB between rows.
+struct FlatRowOperand {
+  const uint16_t* rows[LOADS_PER_THREAD];  // element (row, lchunk * 8) at K = 0
+};
+
+__device__ __forceinline__ void load_stage(const FlatRowOperand& op, int kstep, char* lds_tile, int wave) {
 #pragma unroll
   for (int it = 0; it < LOADS_PER_THREAD; ++it) {
     lds_ptr_t dst = (lds_ptr_t)(lds_tile + (it * NTHREADS + wave * 64) * 16);
     __builtin_amdgcn_global_load_lds((const void*)(op.rows[it] + (size_t)kstep * BK), dst, 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void load_stage(const RowOperand& op, int kstep, char* lds_tile, int wave) {
+  const unsigned soff = __builtin_amdgcn_readfirstlane((unsigned)kstep * BK * 2);
+#pragma unroll
+  for (int it = 0; it < LOADS_PER_THREAD; ++it) {
+    lds_ptr_t dst = (lds_ptr_t)(lds_tile + (it * NTHREADS + wave * 64) * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, dst, 16, op.voff[it], soff, 0, 0);
   }
 }
 __device__ __forceinline__ void load_stage(const TrOperand& op, int kstep, char* lds_tile, int wave) {
@@ -146,6 +185,7 @@ struct TrFrag {
 
 template <typename Op, int NF> struct FragOf;
 template <int NF> struct FragOf<RowOperand, NF> { typedef RowFrag type; };
+template <int NF> struct FragOf<FlatRowOperand, NF> { typedef RowFrag type; };
 template <int NF> struct FragOf<TrOperand, NF> { typedef TrFrag<NF> type; };
 
 // The K loop over nk steps of BK.  nk may be 0 (accumulators stay zero).  The

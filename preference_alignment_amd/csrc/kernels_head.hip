@@ -134,13 +134,14 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
     int mt, nt;
     sc.coords(t, mt, nt);
     const int m0 = mt * BM, n0 = nt * BN;
-    RowOperand wop, hop;
+    // W rows n0 .. n0+255 (rows past V read as zero); hidden rows gathered by
+    // position, addressed from the start of the hidden tensor
+    const RowOperand wop = row_operand(a.w + (size_t)n0 * a.H, a.H, (long)a.V - n0, 0, tid);
+    RowOperand hop;
+    hop.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.hidden, (short)0, (int)a.hidden_bytes, kBufferFlags);
 #pragma unroll
-    for (int it = 0; it < LOADS_PER_THREAD; ++it) {
-      const int r = row_loader_row(it, tid);
-      wop.rows[it] = a.w + (size_t)min(n0 + r, a.V - 1) * a.H + lchunk * 8;
-      hop.rows[it] = a.hidden + (size_t)a.idx[m0 + r] * a.H + lchunk * 8;
-    }
+    for (int it = 0; it < LOADS_PER_THREAD; ++it)
+      hop.voff[it] = (unsigned)(((size_t)a.idx[m0 + row_loader_row(it, tid)] * a.H + lchunk * 8) * 2);
     if (tid < BM) tgt_s[tid] = a.tgt_c[m0 + tid];
     Acc acc;
     mainloop(acc, wop, hop, a.H / BK, smem, wave, lane, wm, wn);
@@ -336,13 +337,14 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
     int mt, nt;
     sc.coords(t, mt, nt);
     const int m0 = mt * BM, n0 = nt * BN;
-    RowOperand wop, hop;
+    // W rows n0 .. n0+255 (rows past V read as zero); hidden rows gathered by
+    // position, addressed from the start of the hidden tensor
+    const RowOperand wop = row_operand(a.w + (size_t)n0 * a.H, a.H, (long)a.V - n0, 0, tid);
+    RowOperand hop;
+    hop.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.hidden, (short)0, (int)a.hidden_bytes, kBufferFlags);
 #pragma unroll
-    for (int it = 0; it < LOADS_PER_THREAD; ++it) {
-      const int r = row_loader_row(it, tid);
-      wop.rows[it] = a.w + (size_t)min(n0 + r, a.V - 1) * a.H + lchunk * 8;
-      hop.rows[it] = a.hidden + (size_t)a.idx[m0 + r] * a.H + lchunk * 8;
-    }
+    for (int it = 0; it < LOADS_PER_THREAD; ++it)
+      hop.voff[it] = (unsigned)(((size_t)a.idx[m0 + row_loader_row(it, tid)] * a.H + lchunk * 8) * 2);
     if (tid < BM) {
       const int m = m0 + tid;
       const bool live = m < n_c;
@@ -420,7 +422,6 @@ __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
   const int nks = cdiv(nkt, a.splitk);
   Sched sc;
   sc.init(cdiv(n_c, BM), nNt * a.splitk, a.gm);
-  const int lchunk = row_lchunk(tid);
   for (int t = sc.begin; t < sc.end; t += sc.step) {
     int mt, ntk;
     sc.coords(t, mt, ntk);
@@ -428,14 +429,16 @@ __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
     const int m0 = mt * BM, n0 = nt * BN;
     const int kb = ks * nks;
     const int nk = max(0, min(nks, nkt - kb));
-    RowOperand dop;
+    FlatRowOperand dop, wop;
+    {
+      const int lchunk = row_lchunk(tid);
 #pragma unroll
-    for (int it = 0; it < LOADS_PER_THREAD; ++it)
-      dop.rows[it] = a.D + (size_t)(m0 + row_loader_row(it, tid)) * a.Vp + (size_t)kb * BK + lchunk * 8;
-    RowOperand wop;
-#pragma unroll
-    for (int it = 0; it < LOADS_PER_THREAD; ++it)
-      wop.rows[it] = a.wt + (size_t)min(n0 + row_loader_row(it, tid), a.H - 1) * a.Vp + (size_t)kb * BK + lchunk * 8;
+      for (int it = 0; it < LOADS_PER_THREAD; ++it) {
+        const int r = row_loader_row(it, tid);
+        dop.rows[it] = a.D + (size_t)(m0 + r) * a.Vp + (size_t)kb * BK + lchunk * 8;
+        wop.rows[it] = a.wt + (size_t)min(n0 + r, a.H - 1) * a.Vp + (size_t)kb * BK + lchunk * 8;
+      }
+    }
     Acc acc;
     mainloop(acc, dop, wop, nk, smem, wave, lane, wm, wn);
     float* part = a.part + (size_t)ks * a.Mp * a.H;
@@ -496,18 +499,12 @@ __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
   const int nk = cdiv(n_c, BK);
   Sched sc;
   sc.init(a.Vp / BM, cdiv(a.H, BN), a.gm);
-  const int lchunk = row_lchunk(tid);
   for (int t = sc.begin; t < sc.end; t += sc.step) {
     int mt, nt;
     sc.coords(t, mt, nt);
     const int m0 = mt * BM, n0 = nt * BN;
-    RowOperand dop, hop;
-#pragma unroll
-    for (int it = 0; it < LOADS_PER_THREAD; ++it) {
-      const int r = row_loader_row(it, tid);
-      dop.rows[it] = a.DT + (size_t)(m0 + r) * a.Mp + lchunk * 8;
-      hop.rows[it] = a.ht + (size_t)min(n0 + r, a.H - 1) * a.Mp + lchunk * 8;
-    }
+    const RowOperand dop = row_operand(a.DT + (size_t)m0 * a.Mp, a.Mp, (long)a.Vp - m0, 0, tid);
+    const RowOperand hop = row_operand(a.ht + (size_t)n0 * a.Mp, a.Mp, (long)a.H - n0, 0, tid);
     Acc acc;
     mainloop(acc, dop, hop, nk, smem, wave, lane, wm, wn);
 #pragma unroll

@@ -25,6 +25,7 @@ struct CompactArgs {
 struct FwdArgs {
   const uint16_t* hidden;  // [rows*T, H]
   const uint16_t* w;       // [V, H]
+  unsigned hidden_bytes;   // rows*T*H*2 (< 4 GiB)
   int H, V, Mp, gm;
   const int* idx;
   const int* tgt_c;
@@ -72,6 +73,7 @@ struct GatherHTArgs {
 struct DProdArgs {
   const uint16_t* hidden;
   const uint16_t* w;
+  unsigned hidden_bytes;  // rows*T*H*2 (< 4 GiB)
   int H, V, Vp, Mp, gm;
   const int* idx;
   const int* tgt_c;

@@ -31,7 +31,7 @@ def test_workspace_sizes(L):
     ok = D.dpo_workspace_bytes(D.DPO_OP_SEQ_LOGPS, 8, 2048, 4096, 128256)
     assert ok > 0
     for args in [(3, 2048, 4096, 128256), (0, 8, 64, 64), (8, 0, 64, 64), (8, 8, 100, 64), (8, 8, 64, 1001),
-                 (8, 8, 0, 64)]:
+                 (8, 8, 0, 64), (256, 4096, 4096, 128256)]:  # last: hidden tensor of 8 GiB
         assert D.dpo_workspace_bytes(D.DPO_OP_SEQ_LOGPS, *args) == 0, args
     assert D.dpo_workspace_bytes(99, 8, 8, 64, 64) == 0
     # logits ops ignore H
