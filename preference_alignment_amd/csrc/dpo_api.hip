@@ -35,7 +35,7 @@ struct Layout {
   size_t hdr = 0, idx = 0, tgt = 0, rowc = 0, rowoff = 0;
   size_t part = 0, tlogit = 0, lse64 = 0, logp64 = 0;
   size_t D = 0, DT = 0, WT = 0, HT = 0;
-  size_t keysA = 0, valsA = 0, keysB = 0, valsB = 0, counters = 0, dhpart = 0, spos = 0, sw = 0, ohcont = 0, ohhead = 0;
+  size_t keysA = 0, valsA = 0, keysB = 0, valsB = 0, dhpart = 0, spos = 0, sw = 0, ohcont = 0, ohhead = 0;
   size_t total = 0;
 };
 
@@ -88,7 +88,6 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     L.valsA = take((size_t)L.Mp * 4);
     L.keysB = take((size_t)L.Mp * 4);
     L.valsB = take((size_t)L.Mp * 4);
-    L.counters = take((size_t)kSortThreads * 256 * 4);
     L.dhpart = take((size_t)kSplitDh * L.Mp * H * 4);
     L.spos = take((size_t)L.Mp * 4);
     L.sw = take((size_t)L.Mp * 4);
@@ -438,7 +437,6 @@ int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int
   so.valsA = at<int>(ws, L.valsA);
   so.keysB = at<int>(ws, L.keysB);
   so.valsB = at<int>(ws, L.valsB);
-  so.counters = at<int>(ws, L.counters);
   so.s_pos = at<int>(ws, L.spos);
   so.s_w = at<float>(ws, L.sw);
   RUN("sort_targets", launch_sort_targets(so, st));

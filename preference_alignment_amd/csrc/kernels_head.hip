@@ -529,51 +529,79 @@ __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
 // one-hot term of dW_vocab: positions sorted by target, then a fixed-order sum
 // ---------------------------------------------------------------------------
 // Stable LSD radix sort (8-bit digits) of the completion positions by target
-// id, in one workgroup.  Each thread owns a contiguous slice of the input, so
-// counting and scattering slice by slice in digit-major order keeps equal
-// keys in ascending position order.  Out-of-range targets (-1) sort last.
+// id, in one workgroup of 16 waves.  Each wave owns a contiguous slice of the
+// input; per pass it counts its digits (LDS), the counts are scanned
+// digit-major / wave-minor, and each wave scatters its slice 64 keys at a
+// time: a key's rank among equal digits of its 64-key chunk comes from 8
+// ballots (the lanes sharing all 8 digit bits), so equal keys keep their
+// input order.  Out-of-range targets (-1) sort last.  Afterwards every sorted
+// entry gets its flat position and row weight, for k_onehot_dw.
+constexpr int kSortWaves = kSortThreads / 64;
+
 __global__ __launch_bounds__(kSortThreads) void k_sort_targets(SortArgs a) {
+  __shared__ int cnt[kSortWaves][256];
   __shared__ int dig_base[256];
-  __shared__ int dig_tot[256];
   const int n = a.hdr->n_c;
   const int tid = threadIdx.x;
-  const int per = cdiv(n, kSortThreads);
-  const int lo = min(n, per * tid), hi = min(n, lo + per);
-  int* cnt = a.counters + tid * 256;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int per = cdiv(n, kSortWaves);
+  const int lo = min(n, per * wave), hi = min(n, lo + per);
+  const unsigned long long below = (1ull << lane) - 1ull;
   const int* kin = a.tgt_c;
   const int* vin = nullptr;
   int* kout = a.keysB;
   int* vout = a.valsB;
   for (int p = 0; p < a.passes; ++p) {
     const int shift = 8 * p;
-    for (int d = 0; d < 256; ++d) cnt[d] = 0;
-    for (int i = lo; i < hi; ++i) cnt[((unsigned)kin[i] >> shift) & 255u] += 1;
+#pragma unroll
+    for (int d = lane; d < 256; d += 64) cnt[wave][d] = 0;
+    __syncthreads();
+    for (int base = lo; base < hi; base += 64) {
+      const int i = base + lane;
+      if (i < hi) atomicAdd(&cnt[wave][((unsigned)kin[i] >> shift) & 255u], 1);
+    }
     __syncthreads();
     if (tid < 256) {
       int run = 0;
-      for (int t = 0; t < kSortThreads; ++t) {
-        int* c = a.counters + t * 256 + tid;
-        const int v = *c;
-        *c = run;
-        run += v;
+      for (int w = 0; w < kSortWaves; ++w) {
+        const int c = cnt[w][tid];
+        cnt[w][tid] = run;
+        run += c;
       }
-      dig_tot[tid] = run;
+      dig_base[tid] = run;  // digit total for now
     }
     __syncthreads();
     if (tid == 0) {
       int run = 0;
       for (int d = 0; d < 256; ++d) {
+        const int c = dig_base[d];
         dig_base[d] = run;
-        run += dig_tot[d];
+        run += c;
       }
     }
     __syncthreads();
-    for (int i = lo; i < hi; ++i) {
-      const int k = kin[i];
+    for (int base = lo; base < hi; base += 64) {
+      const int i = base + lane;
+      const bool valid = i < hi;
+      const int k = valid ? kin[i] : 0;
       const int d = ((unsigned)k >> shift) & 255u;
-      const int o = dig_base[d] + cnt[d]++;
-      kout[o] = k;
-      vout[o] = vin ? vin[i] : i;
+      const unsigned long long vmask = __ballot(valid);
+      unsigned long long peers = vmask;
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const bool set = (d >> bit) & 1;
+        const unsigned long long bb = __ballot(valid && set);
+        peers &= set ? bb : (vmask & ~bb);
+      }
+      const int rank = __popcll(peers & below);
+      const int slot = valid ? dig_base[d] + cnt[wave][d] + rank : 0;
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        kout[slot] = k;
+        vout[slot] = vin ? vin[i] : i;
+        if (rank == 0) cnt[wave][d] += __popcll(peers);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
     kin = kout;
@@ -582,7 +610,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_targets(SortArgs a) {
     vout = (vout == a.valsB) ? a.valsA : a.valsB;
   }
   // per sorted entry: flat position and row weight, read by k_onehot_dw
-  for (int i = lo; i < hi; ++i) {
+  for (int i = tid; i < n; i += kSortThreads) {
     const int m = vin[i];
     a.s_pos[i] = a.idx[m];
     a.s_w[i] = a.weight[a.row_c[m]];

@@ -116,7 +116,6 @@ struct SortArgs {
   int* valsA;
   int* keysB;
   int* valsB;
-  int* counters;        // [kSortThreads * 256]
   int* s_pos;           // [n_c] flat position of each sorted entry
   float* s_w;           // [n_c] its row weight
 };
@@ -194,7 +193,7 @@ hipError_t launch_dw_gemm(const DwArgs& a, int grid, hipStream_t s);
 hipError_t launch_zero_rows(const ZeroRowsArgs& a, long positions, hipStream_t s);
 hipError_t launch_sort_targets(const SortArgs& a, hipStream_t s);
 hipError_t launch_onehot_dw(const OnehotDwArgs& a, int Mp, hipStream_t s);
-constexpr int kSortThreads = 512;
+constexpr int kSortThreads = 1024;
 hipError_t launch_stream_fwd(const StreamFwdArgs& a, long positions, hipStream_t s);
 hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, hipStream_t s);
 hipError_t launch_reset_status(WsHeader* hdr, hipStream_t s);
