@@ -37,6 +37,52 @@ METRICS = {
 }
 
 
+# Kernel families whose sources decide a kernel's HBM traffic; the counter
+# table under profiles/ records the digest of the family it was measured on.
+CSRC = os.path.join(ROOT, "preference_alignment_amd", "csrc")
+FAMILIES = {"head": ["dpo_common.h", "gemm_core.h", "kernels_head.hip", "launch.h"],
+            "stream": ["dpo_common.h", "kernels_stream.hip", "launch.h"]}
+KERNEL_FAMILY = {"fwd_gemm": "head", "dlogits_gemm": "head", "dhidden_gemm": "head", "dw_gemm": "head",
+                 "stream_fwd": "stream", "stream_bwd": "stream"}
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+
+
+def source_digest(family):
+    import hashlib
+    h = hashlib.sha256()
+    for n in FAMILIES[family]:
+        h.update(n.encode()); h.update(b"\0")
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE counters,
+    scaled by the copy calibration; None when absent or when the kernel's
+    sources changed since the counters were taken."""
+    fam = KERNEL_FAMILY.get(kernel)
+    if fam is None or not os.path.exists(TRAFFIC_TABLE):
+        return None
+    scale = {}
+    rows = {}
+    with open(TRAFFIC_TABLE) as f:
+        for line in f:
+            line = line.strip()
+            for key in ("fetch_scale", "write_scale"):
+                if line.startswith(key + ":"):
+                    scale[key] = float(line.split(":", 1)[1])
+            if line.startswith("|") and not line.startswith("|---"):
+                c = [x.strip() for x in line.strip("|").split("|")]
+                if len(c) >= 6 and c[0] in KERNEL_FAMILY and c[1].isdigit():
+                    rows[(c[0], int(c[1]))] = (c[2], c[3], float(c[4]), float(c[5]))
+    r = rows.get((kernel, workload))
+    if r is None or len(scale) != 2 or r[0] != fam or r[1] != source_digest(fam):
+        return None
+    return (r[2] * scale["fetch_scale"] + r[3] * scale["write_scale"]) * 1024.0
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -225,10 +271,11 @@ def main():
         E = x.rows * x.T * V
         per_kernel_bytes = {"stream_fwd": n_c * V * 2.0, "stream_bwd": n_c * V * 2.0 + E * 2.0}
         dom = max(per_kernel_bytes, key=lambda k: kern_avg.get(k, (0,))[0]) if kern_avg else "stream_bwd"
-        avg = kern_avg.get(dom, (float("nan"), 0))[0]
-        ach = per_kernel_bytes[dom] / (avg / 1e3) / 1e9
+        avg = kern_avg[dom][0] if dom in kern_avg else None
+        ach = per_kernel_bytes[dom] / (avg / 1e3) / 1e9 if avg else None
         roof = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": ach / PEAK_HBM_GBS, "traffic": None, "avg_ms": avg,
+                "frac": ach / PEAK_HBM_GBS if ach else None,
+                "traffic": measured_traffic(dom, a.workload), "avg_ms": avg,
                 "algorithmic_bytes_per_launch": per_kernel_bytes[dom]}
         step_bytes = n_c * V * 2.0 * 2 + E * 2.0
         extra = {"step_hbm_frac": step_bytes / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS}
@@ -236,10 +283,11 @@ def main():
         gemms = ["fwd_gemm"] if a.workload == 3 else ["fwd_gemm", "dlogits_gemm", "dhidden_gemm", "dw_gemm"]
         flops = 2.0 * n_c * H * V
         dom = max(gemms, key=lambda k: kern_avg.get(k, (0,))[0]) if kern_avg else gemms[0]
-        avg = kern_avg.get(dom, (float("nan"), 0))[0]
-        ach = flops / (avg / 1e3) / 1e12
+        avg = kern_avg[dom][0] if dom in kern_avg else None
+        ach = flops / (avg / 1e3) / 1e12 if avg else None
         roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "avg_ms": avg,
+                "frac": ach / PEAK_BF16_TFLOPS if ach else None,
+                "traffic": measured_traffic(dom, a.workload), "avg_ms": avg,
                 "algorithmic_flops_per_launch": flops}
         step_flops = flops * len(gemms)
         extra = {"step_mfma_frac": step_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
