@@ -181,6 +181,111 @@ def logits_seq_logps(logits_bits, targets, mask, chunk: int = 256) -> Dict[str, 
                 logp=logp.reshape(R, T), n_tokens=n_tokens, idx=idx)
 
 
+def logits_f32_seq_logps(logits_f32, targets, mask, chunk: int = 256) -> Dict[str, np.ndarray]:
+    """Sequence scores from float32 logits [R,T,V] ("DPO Training on GPU, in
+    depth", "Where the memory goes": fp32 logits of a 2,048-token sequence at
+    V = 128,256 take 0.98 GiB).  float32 widens to float64 exactly."""
+    return logits_seq_logps_f64(np.asarray(logits_f32, dtype=np.float32).astype(np.float64),
+                                targets, mask, chunk)
+
+
+# ----------------------------------------------------------------------------
+# a vocabulary shard's share of the log-sum-exp (tensor parallelism over V:
+# the Megatron-Bridge change scores with TP=4 and notes that sums change with
+# the shard count; "DPO Training on GPU, in depth", "A training configuration
+# that fits": the log-softmax spans the whole vocabulary)
+# ----------------------------------------------------------------------------
+def shard_partials_f64(hidden: np.ndarray, w_shard: np.ndarray, targets: np.ndarray,
+                       mask: np.ndarray, v_begin: int, V_total: int, chunk: int = 256
+                       ) -> Dict[str, np.ndarray]:
+    """For the logits z[v] = W[v] . h, v in [v_begin, v_begin + V_shard), at
+    every completion position: the shard maximum m, the shard sum of
+    exp(z - m), and the target logit when the target lies in the shard.
+
+    All outputs are [R, T]; positions outside the mask, and target logits of
+    targets held by another shard, are (-inf, 0, -inf).
+    """
+    R, T, H = hidden.shape
+    Vs = w_shard.shape[0]
+    idx, _ = completion_positions(mask)
+    tflat = np.asarray(targets).reshape(-1).astype(np.int64)
+    _check_targets(tflat[idx], V_total)
+    hflat = hidden.reshape(R * T, H)
+    pmax = np.full(R * T, -np.inf)
+    psum = np.zeros(R * T)
+    ptgt = np.full(R * T, -np.inf)
+    for s in range(0, idx.size, chunk):
+        c = idx[s:s + chunk]
+        Z = hflat[c] @ w_shard.T
+        m = Z.max(axis=1)
+        pmax[c] = m
+        psum[c] = np.exp(Z - m[:, None]).sum(axis=1)
+        y = tflat[c] - v_begin
+        inside = np.flatnonzero((y >= 0) & (y < Vs))
+        ptgt[c[inside]] = Z[inside, y[inside]]
+    return dict(max=pmax.reshape(R, T), sumexp=psum.reshape(R, T), tgt=ptgt.reshape(R, T))
+
+
+def combine_shards(part_max: np.ndarray, part_sumexp: np.ndarray, part_tgt: np.ndarray,
+                   mask: np.ndarray) -> Dict[str, np.ndarray]:
+    """Whole-vocabulary lse and scores from S shards' partials [S, R, T]:
+    lse = M + log(sum_s sumexp_s * exp(max_s - M)) with M = max_s max_s; the
+    target logit is the one shard's finite value; log p = target - lse."""
+    pm = np.asarray(part_max, dtype=np.float64)
+    ps = np.asarray(part_sumexp, dtype=np.float64)
+    pt = np.asarray(part_tgt, dtype=np.float64)
+    S, R, T = pm.shape
+    idx, n_tokens = completion_positions(mask)
+    pm = pm.reshape(S, R * T)[:, idx]
+    ps = ps.reshape(S, R * T)[:, idx]
+    pt = pt.reshape(S, R * T)[:, idx]
+    M = pm.max(axis=0)
+    scaled = np.where(np.isfinite(pm), ps * np.exp(np.where(np.isfinite(pm), pm - M, 0.0)), 0.0)
+    lse_c = M + np.log(scaled.sum(axis=0))
+    tgt = pt.max(axis=0)
+    if idx.size and not np.all(np.isfinite(tgt)):
+        raise ValueError("a completion position has no shard holding its target")
+    lse = np.zeros(R * T)
+    logp = np.zeros(R * T)
+    lse[idx] = lse_c
+    logp[idx] = tgt - lse_c
+    return dict(logp_sum=_row_sums(logp, idx, R, T), lse=lse.reshape(R, T),
+                logp=logp.reshape(R, T), n_tokens=n_tokens, idx=idx)
+
+
+# ----------------------------------------------------------------------------
+# forward by-product: logits sums for the logits-mean metrics ("Run
+# Distributed Full-Model DPO with PyTorch FSDP", "Common Pitfalls": the loop
+# logs the mean chosen and rejected logits, then frees the logits)
+# ----------------------------------------------------------------------------
+def logit_row_sums_f64(hidden: np.ndarray, w: np.ndarray, mask: np.ndarray,
+                       chunk: int = 256) -> np.ndarray:
+    """Per row: the sum of all V logits over the row's completion positions."""
+    R, T, H = hidden.shape
+    idx, _ = completion_positions(mask)
+    hflat = hidden.reshape(R * T, H)
+    tot = np.zeros(R * T)
+    for s in range(0, idx.size, chunk):
+        c = idx[s:s + chunk]
+        tot[c] = (hflat[c] @ w.T).sum(axis=1)
+    rows = idx // T
+    return np.array([math.fsum(tot[idx[rows == r]].tolist()) for r in range(R)])
+
+
+def logits_means(logit_sum: np.ndarray, n_tokens: np.ndarray, V: int,
+                 layout: int = PAIRS_ADJACENT) -> Tuple[float, float]:
+    """Mean logit over the completion positions and the vocabulary of the
+    chosen rows and of the rejected rows (0 for a half without tokens)."""
+    ls = np.asarray(logit_sum, dtype=np.float64)
+    n = np.asarray(n_tokens, dtype=np.int64)
+    c, r = pair_rows(ls.size // 2, layout)
+    out = []
+    for rows in (c, r):
+        cnt = int(n[rows].sum())
+        out.append(math.fsum(ls[rows].tolist()) / (cnt * V) if cnt else 0.0)
+    return out[0], out[1]
+
+
 # ----------------------------------------------------------------------------
 # the sigmoid DPO loss
 # ----------------------------------------------------------------------------
@@ -234,6 +339,65 @@ def dpo_loss(policy_sum: np.ndarray, ref_sum: np.ndarray, beta: float,
     weight[r] = -beta * s / B
     return dict(loss=loss, weight=weight, reward=reward, margin=margin,
                 accuracy=float(np.mean(margin > 0)), sig_neg_margin=s)
+
+
+def dpo_loss_variant(policy_sum: np.ndarray, ref_sum, n_tokens, beta: float,
+                     layout: int = PAIRS_ADJACENT, length_normalise: bool = False,
+                     reference_free: bool = False, sft_alpha: float = 0.0
+                     ) -> Dict[str, np.ndarray]:
+    """The sigmoid loss with the variants the pages name, on the same row scores.
+
+    * reference-free ("Run Distributed Full-Model DPO with PyTorch FSDP",
+      "Where to Go Next": the loop checks whether the objective is
+      reference-free, which drops the reference model): reference scores are 0.
+    * length-normalised ("DPO Training on GPU, in depth", "Failure modes you
+      will see on real runs": sigmoid_norm against length exploitation; the
+      FSDP page, "Step 4", passes sums so that the loss can average): each
+      row's policy and reference scores are divided by the row's completion
+      token count; a row without completion tokens averages to 0.
+    * SFT / NLL term on chosen rows ("Direct Preference Optimization (DPO):
+      End-to-End Implementation": total = DPO loss + alpha * NLL on the chosen
+      responses, alpha called RPO alpha; "DPO Training on GPU, in depth": the
+      sigmoid + sft multi-loss; the Megatron-Bridge change: optional SFT term):
+      NLL = mean negative log-probability per chosen completion token of the
+      batch = -sum(pi_c) / sum(n_c), 0 when the chosen rows hold no tokens.
+
+    weight = -d loss / d pi per row, as for ``dpo_loss``.
+    """
+    if not (np.isfinite(beta) and beta > 0):
+        raise ValueError("beta must be finite and positive")
+    if not (np.isfinite(sft_alpha) and sft_alpha >= 0):
+        raise ValueError("sft_alpha must be finite and non-negative")
+    pi = np.asarray(policy_sum, dtype=np.float64)
+    R = pi.size
+    if R % 2 or R == 0:
+        raise ValueError("rows must be even and positive")
+    B = R // 2
+    ref = np.zeros(R) if reference_free else np.asarray(ref_sum, dtype=np.float64)
+    n = np.asarray(n_tokens, dtype=np.int64) if n_tokens is not None else None
+    if (length_normalise or sft_alpha > 0) and n is None:
+        raise ValueError("token counts are needed for length normalisation and the NLL term")
+    if length_normalise:
+        scale = np.where(n > 0, 1.0 / np.maximum(n, 1), 0.0)
+    else:
+        scale = np.ones(R)
+    c, r = pair_rows(B, layout)
+    reward = beta * (pi - ref) * scale
+    margin = reward[c] - reward[r]
+    pref = float(np.mean(softplus(-margin)))
+    s = sigmoid(-margin)
+    weight = np.zeros(R)
+    weight[c] = beta * s * scale[c] / B
+    weight[r] = -beta * s * scale[r] / B
+    nll = 0.0
+    if sft_alpha > 0 or n is not None:
+        n_ch = int(n[c].sum()) if n is not None else 0
+        if n_ch > 0:
+            nll = -math.fsum(pi[c].tolist()) / n_ch
+            if sft_alpha > 0:
+                weight[c] += sft_alpha / n_ch
+    return dict(loss=pref + sft_alpha * nll, pref_loss=pref, nll=nll, weight=weight, reward=reward,
+                margin=margin, accuracy=float(np.mean(margin > 0)), sig_neg_margin=s)
 
 
 # ----------------------------------------------------------------------------
@@ -298,6 +462,55 @@ def logits_backward_rows(logits_bits, targets, mask, lse, weight, flat_positions
         p = pos[live]
         _check_targets(tflat[p], V)
         P = np.exp(bf16_to_f64(lflat[p]) - lse_flat[p][:, None])
+        P[np.arange(p.size), tflat[p]] -= 1.0
+        out[live] = _row_weight(weight, p, T)[:, None] * P
+    return out
+
+
+def head_backward_shard_f64(hidden: np.ndarray, w_shard: np.ndarray, targets: np.ndarray,
+                            mask: np.ndarray, lse: np.ndarray, weight: np.ndarray, v_begin: int,
+                            V_total: int, chunk: int = 256) -> Tuple[np.ndarray, np.ndarray]:
+    """One vocabulary shard's part of the head gradient: with the whole-vocabulary
+    lse, d loss / d z[t, v] = w_r (softmax[v] - [v == y]) for v in the shard;
+    returns this shard's dHidden term (the shards' terms add up to dHidden) and
+    dW for the shard's rows."""
+    R, T, H = hidden.shape
+    Vs = w_shard.shape[0]
+    idx, _ = completion_positions(mask)
+    tflat = np.asarray(targets).reshape(-1).astype(np.int64)
+    _check_targets(tflat[idx], V_total)
+    hflat = hidden.reshape(R * T, H)
+    lse_flat = np.asarray(lse, dtype=np.float64).reshape(-1)
+    wrow = _row_weight(weight, idx, T)
+    dH = np.zeros((R * T, H))
+    dW = np.zeros((Vs, H))
+    for s in range(0, idx.size, chunk):
+        c = idx[s:s + chunk]
+        Hc = hflat[c]
+        P = np.exp(Hc @ w_shard.T - lse_flat[c][:, None])
+        y = tflat[c] - v_begin
+        inside = np.flatnonzero((y >= 0) & (y < Vs))
+        P[inside, y[inside]] -= 1.0
+        D = wrow[s:s + chunk][:, None] * P
+        dH[c] = D @ w_shard
+        dW += D.T @ Hc
+    return dH.reshape(R, T, H), dW
+
+
+def logits_f32_backward_rows(logits_f32, targets, mask, lse, weight, flat_positions) -> np.ndarray:
+    """As ``logits_backward_rows`` for float32 logits."""
+    R, T, V = logits_f32.shape
+    pos = np.asarray(flat_positions, dtype=np.int64)
+    lflat = np.asarray(logits_f32, dtype=np.float32).reshape(R * T, V)
+    m = np.asarray(mask).reshape(-1) != 0
+    tflat = np.asarray(targets).reshape(-1).astype(np.int64)
+    lse_flat = np.asarray(lse, dtype=np.float64).reshape(-1)
+    out = np.zeros((pos.size, V))
+    live = np.flatnonzero(m[pos])
+    if live.size:
+        p = pos[live]
+        _check_targets(tflat[p], V)
+        P = np.exp(lflat[p].astype(np.float64) - lse_flat[p][:, None])
         P[np.arange(p.size), tflat[p]] -= 1.0
         out[live] = _row_weight(weight, p, T)[:, None] * P
     return out
