@@ -60,7 +60,8 @@ enum {
   DPO_ERR_LAYOUT = -5,       /* unknown pair layout / flag value */
   DPO_ERR_WORKSPACE = -6,    /* workspace smaller than dpo_workspace_bytes() */
   DPO_ERR_TARGET_RANGE = -7, /* device-detected target id outside [0, V) */
-  DPO_ERR_HIP = -8           /* a HIP runtime call failed */
+  DPO_ERR_HIP = -8,          /* a HIP runtime call failed */
+  DPO_ERR_ALPHA = -9         /* sft_alpha is not finite and >= 0 */
 };
 
 /* Pair layouts of the concatenated batch.
@@ -78,9 +79,18 @@ enum {
   DPO_OP_SEQ_LOGPS = 0,
   DPO_OP_REF_SCORE = 1,
   DPO_OP_HEAD_BACKWARD = 2,
-  DPO_OP_LOGITS_SEQ_LOGPS = 3,
-  DPO_OP_LOGITS_BACKWARD = 4
+  DPO_OP_LOGITS_SEQ_LOGPS = 3, /* also the fp32-logits forward */
+  DPO_OP_LOGITS_BACKWARD = 4,  /* also the fp32-logits backward */
+  DPO_OP_SHARD_COMBINE = 5,    /* dpo_shard_combine; V = the whole vocabulary */
+  DPO_OP_SEQ_LOGPS_METRICS = 6 /* dpo_seq_logps_metrics */
 };
+/* The vocabulary-shard entry points take the workspace of the unsharded
+ * operation at the shard's size: dpo_workspace_bytes(DPO_OP_SEQ_LOGPS, ...,
+ * V_shard) for dpo_seq_logps_shard and (DPO_OP_HEAD_BACKWARD, ..., V_shard)
+ * for dpo_head_backward_shard. */
+
+/* Flags of dpo_loss_ex. */
+enum { DPO_LOSS_LENGTH_NORM = 1, DPO_LOSS_REFERENCE_FREE = 2 };
 
 /* Bytes of device workspace `op` needs for these sizes (H is ignored by the
  * logits operations).  Returns 0 if the sizes break the shape rules or `op`
@@ -135,6 +145,33 @@ int dpo_loss(const double* policy_sum64, const float* ref_sum, int num_pairs, do
              int layout, float* loss, float* weight, float* reward, float* margin,
              float* accuracy, void* stream);
 
+/* The loss variants the pages name, on the same scores and weights; the
+ * backward entry points take the resulting `weight` unchanged.
+ *  - DPO_LOSS_REFERENCE_FREE: reference scores are 0 and ref_sum may be NULL
+ *    ("Run Distributed Full-Model DPO with PyTorch FSDP", "Where to Go
+ *    Next": a reference-free objective drops the reference model).
+ *  - DPO_LOSS_LENGTH_NORM: every row's policy and reference score is divided
+ *    by its completion token count n_tokens[r] before the margin ("DPO
+ *    Training on GPU, in depth", "Failure modes you will see on real runs":
+ *    length-normalised variants such as sigmoid_norm); a row without tokens
+ *    averages to 0 and gets weight 0.
+ *  - sft_alpha > 0: loss += sft_alpha * NLL with NLL = -sum(policy of chosen
+ *    rows) / sum(n_tokens of chosen rows), the mean negative log-probability
+ *    per chosen completion token of the batch ("Direct Preference
+ *    Optimization (DPO): End-to-End Implementation": DPO loss plus RPO alpha
+ *    times the NLL on the chosen responses; the Megatron-Bridge change's
+ *    optional SFT term).  Every chosen row's weight grows by
+ *    sft_alpha / sum(n_tokens of chosen rows).
+ *   n_tokens [2B] int32: required for LENGTH_NORM, sft_alpha > 0 or a
+ *     non-NULL nll; the counts dpo_seq_logps wrote.
+ *   nll [1] float, nullable: the NLL value (also when sft_alpha == 0).
+ *   loss = preference loss + sft_alpha * NLL; other outputs as dpo_loss.
+ * Errors: unknown flag bits -> DPO_ERR_LAYOUT; bad sft_alpha -> DPO_ERR_ALPHA. */
+int dpo_loss_ex(const double* policy_sum64, const float* ref_sum, const int32_t* n_tokens,
+                int num_pairs, double beta, int layout, int flags, double sft_alpha, float* loss,
+                float* weight, float* reward, float* margin, float* accuracy, float* nll,
+                void* stream);
+
 /* Head gradients of the loss through the row scores:
  *   D_{r,t} = weight_r (softmax(W h_{r,t}) - onehot(y_{r,t}))   at completion positions
  *   d_hidden[r,t,:] = D_{r,t} W      (exactly 0 at mask-0 positions)
@@ -162,6 +199,78 @@ int dpo_logits_backward(const dpo_bf16* logits, const int32_t* targets, const ui
                         int rows, int T, int V, const float* lse, const float* weight,
                         dpo_bf16* d_logits, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* The same two streaming passes over fp32 logits ("DPO Training on GPU, in
+ * depth", "Where the memory goes for an 8B model": fp32 logits of a
+ * 2,048-token sequence take 0.98 GiB).  logits [rows, T, V] float; the
+ * backward writes d_logits [rows, T, V] float (no rounding), 0 at mask-0
+ * positions.  Workspaces: DPO_OP_LOGITS_SEQ_LOGPS / DPO_OP_LOGITS_BACKWARD. */
+int dpo_logits_f32_seq_logps(const float* logits, const int32_t* targets, const uint8_t* mask,
+                             int rows, int T, int V, float* logp_sum, double* logp_sum64,
+                             float* lse, int32_t* n_tokens, void* workspace,
+                             size_t workspace_bytes, void* stream);
+int dpo_logits_f32_backward(const float* logits, const int32_t* targets, const uint8_t* mask,
+                            int rows, int T, int V, const float* lse, const float* weight,
+                            float* d_logits, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* One GPU's share of a head whose vocabulary is split over GPUs (tensor
+ * parallelism over W_vocab rows; the Megatron-Bridge change scores and trains
+ * with TP=4 and notes that the sums change with the shard count).  This GPU
+ * holds W rows [v_begin, v_begin + V_shard) of a V_total vocabulary as
+ * w_shard [V_shard, H] (V_shard % 8 == 0, v_begin >= 0,
+ * v_begin + V_shard <= V_total).  Targets are global ids in [0, V_total).
+ *
+ * dpo_seq_logps_shard writes, for every position (layout [rows, T], float):
+ *   part_max     max over the shard's logits   (-inf at mask-0 positions)
+ *   part_sumexp  sum over the shard of exp(z - part_max)   (0 at mask-0)
+ *   part_tgt     the target's logit if this shard holds the target, else -inf
+ * A caller gathers the S shards' arrays into [S, rows, T] (one all-gather of
+ * 12 bytes per position) and calls dpo_shard_combine, which forms
+ *   lse = M + log(sum_s part_sumexp_s exp(part_max_s - M)),  M = max_s part_max_s
+ *   log p = (the one finite part_tgt) - lse
+ * in fp64 and writes the same outputs as dpo_seq_logps.  A completion
+ * position that no shard holds the target of is reported through
+ * dpo_device_status as DPO_ERR_TARGET_RANGE.
+ *
+ * dpo_head_backward_shard takes the combined lse and the loss weights and
+ * writes this shard's share: d_hidden [rows, T, H] fp32 is the shard's term
+ * D_shard W_shard (the shards' terms add up to the whole dHidden: one
+ * all-reduce), d_w_shard [V_shard, H] fp32 the shard's rows of dW_vocab.
+ * The one-hot part of D applies only where this shard holds the target. */
+int dpo_seq_logps_shard(const dpo_bf16* hidden, const dpo_bf16* w_shard, const int32_t* targets,
+                        const uint8_t* mask, int rows, int T, int H, int V_shard, int v_begin,
+                        int V_total, float* part_max, float* part_sumexp, float* part_tgt,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int dpo_shard_combine(const float* part_max, const float* part_sumexp, const float* part_tgt,
+                      int num_shards, const int32_t* targets, const uint8_t* mask, int rows, int T,
+                      int V_total, float* logp_sum, double* logp_sum64, float* lse,
+                      int32_t* n_tokens, void* workspace, size_t workspace_bytes, void* stream);
+int dpo_head_backward_shard(const dpo_bf16* hidden, const dpo_bf16* w_shard,
+                            const int32_t* targets, const uint8_t* mask, int rows, int T, int H,
+                            int V_shard, int v_begin, int V_total, const float* lse,
+                            const float* weight, float* d_hidden, float* d_w_shard,
+                            int accumulate_dw, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Forward by-products for the logits-mean metrics ("Run Distributed
+ * Full-Model DPO with PyTorch FSDP", "What to Watch Out For": the loop logs the
+ * mean chosen and rejected logits and then frees the logits).  Here the
+ * logits never exist, so the forward epilogue sums them on the way:
+ * dpo_seq_logps_metrics is dpo_seq_logps plus
+ *   logit_sum [rows] double = sum over the row's completion positions and all
+ *                             V vocabulary entries of the logits
+ * (workspace DPO_OP_SEQ_LOGPS_METRICS).  dpo_logits_mean turns the sums into
+ *   means[0] = mean logit of the chosen rows, means[1] = of the rejected rows,
+ * each over (completion positions x V); 0 for a half without tokens.  The
+ * pages average over the whole logits tensor; this build has logits only at
+ * completion positions, so the means cover those. */
+int dpo_seq_logps_metrics(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t* targets,
+                          const uint8_t* mask, int rows, int T, int H, int V, float* logp_sum,
+                          double* logp_sum64, float* lse, int32_t* n_tokens, double* logit_sum,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int dpo_logits_mean(const double* logit_sum, const int32_t* n_tokens, int num_pairs, int V,
+                    int layout, float* means, void* stream);
 
 /* Waits for `stream`, then returns DPO_ERR_TARGET_RANGE if the most recent
  * call that used `workspace` met a target id outside [0, V) at a completion

@@ -255,7 +255,7 @@ def combine_shards(part_max: np.ndarray, part_sumexp: np.ndarray, part_tgt: np.n
 
 # ----------------------------------------------------------------------------
 # forward by-product: logits sums for the logits-mean metrics ("Run
-# Distributed Full-Model DPO with PyTorch FSDP", "Common Pitfalls": the loop
+# Distributed Full-Model DPO with PyTorch FSDP", "What to Watch Out For": the loop
 # logs the mean chosen and rejected logits, then frees the logits)
 # ----------------------------------------------------------------------------
 def logit_row_sums_f64(hidden: np.ndarray, w: np.ndarray, mask: np.ndarray,

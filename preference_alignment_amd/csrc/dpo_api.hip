@@ -33,11 +33,18 @@ struct Layout {
   int Vp = 0;   // vocabulary rounded up to the GEMM tile
   int nVt = 0;  // vocabulary tiles of the forward contraction
   size_t hdr = 0, idx = 0, tgt = 0, rowc = 0, rowoff = 0;
-  size_t part = 0, tlogit = 0, lse64 = 0, logp64 = 0;
+  size_t part = 0, tlogit = 0, lse64 = 0, logp64 = 0, partz = 0, zsum64 = 0;
   size_t D = 0, DT = 0, WT = 0, HT = 0;
   size_t keysA = 0, valsA = 0, keysB = 0, valsB = 0, dhpart = 0, spos = 0, sw = 0, ohcont = 0, ohhead = 0;
   size_t total = 0;
 };
+
+bool op_needs_h(int op) {
+  return op == DPO_OP_SEQ_LOGPS || op == DPO_OP_REF_SCORE || op == DPO_OP_HEAD_BACKWARD ||
+         op == DPO_OP_SEQ_LOGPS_METRICS;
+}
+
+bool op_known(int op) { return op >= DPO_OP_SEQ_LOGPS && op <= DPO_OP_SEQ_LOGPS_METRICS; }
 
 bool shape_ok(int rows, int T, int H, int V, bool need_h) {
   if (rows <= 0 || (rows & 1) || T <= 0 || V <= 0 || (V % 8)) return false;
@@ -71,9 +78,14 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
   L.tgt = take((size_t)L.Mp * 4);
   L.rowc = take((size_t)L.Mp * 4);
   L.rowoff = take((size_t)(rows + 1) * 4);
-  if (op == DPO_OP_SEQ_LOGPS || op == DPO_OP_REF_SCORE) {
+  const bool fwd = op == DPO_OP_SEQ_LOGPS || op == DPO_OP_REF_SCORE || op == DPO_OP_SEQ_LOGPS_METRICS;
+  if (fwd) {
     L.part = take((size_t)L.nVt * L.Mp * sizeof(float2));
     L.tlogit = take((size_t)L.Mp * 4);
+  }
+  if (op == DPO_OP_SEQ_LOGPS_METRICS) {
+    L.partz = take((size_t)L.nVt * L.Mp * 4);
+    L.zsum64 = take((size_t)L.Mp * 8);
   }
   if (op != DPO_OP_HEAD_BACKWARD) {
     L.lse64 = take((size_t)L.Mp * 8);
@@ -209,14 +221,32 @@ int check_common(const void* targets, const void* mask, int rows, int T, int H, 
   return DPO_OK;
 }
 
+// Vocabulary slice a call works on: rows [v_begin, v_begin + V) of a
+// vocabulary of V_total (the whole vocabulary: v_begin = 0, V_total = V).
+struct VocabSlice {
+  int v_begin, V_total;
+};
+
+struct OffMask {
+  float* max = nullptr;
+  float* sum = nullptr;
+  float* tgt = nullptr;
+};
+
 int enqueue_compact(const Layout& L, void* ws, const int32_t* targets, const uint8_t* mask, int rows,
-                    int T, int V, float* lse_out, hipStream_t st) {
+                    int T, int V, float* lse_out, hipStream_t st, VocabSlice vs = {0, -1},
+                    OffMask off = OffMask()) {
   CompactArgs c;
   c.mask = mask;
   c.targets = targets;
   c.rows = rows;
   c.T = T;
   c.V = V;
+  c.v_begin = vs.v_begin;
+  c.V_total = vs.V_total < 0 ? V : vs.V_total;
+  c.off_max = off.max;
+  c.off_sum = off.sum;
+  c.off_tgt = off.tgt;
   c.Mp = L.Mp;
   c.hdr = at<WsHeader>(ws, L.hdr);
   c.idx = at<int>(ws, L.idx);
@@ -228,14 +258,13 @@ int enqueue_compact(const Layout& L, void* ws, const int32_t* targets, const uin
   return DPO_OK;
 }
 
-int enqueue_fused_forward(const dpo_bf16* hidden, const dpo_bf16* w, const int32_t* targets,
-                          const uint8_t* mask, int rows, int T, int H, int V, float* sum32,
-                          double* sum64, float* lse, int32_t* n_tokens, void* ws, int op,
-                          hipStream_t st) {
+// compaction + the forward contraction; leaves per-tile partials in the workspace
+int enqueue_forward_tiles(const dpo_bf16* hidden, const dpo_bf16* w, const int32_t* targets,
+                          const uint8_t* mask, int rows, int T, int H, int V, float* lse, void* ws,
+                          int op, hipStream_t st, VocabSlice vs, OffMask off, FwdArgs& f) {
   const Layout L = make_layout(op, rows, T, H, V);
-  int rc = enqueue_compact(L, ws, targets, mask, rows, T, V, lse, st);
+  int rc = enqueue_compact(L, ws, targets, mask, rows, T, V, lse, st, vs, off);
   if (rc) return rc;
-  FwdArgs f;
   f.hidden = hidden;
   f.w = w;
   f.hidden_bytes = (unsigned)((size_t)rows * T * H * 2);
@@ -248,7 +277,20 @@ int enqueue_fused_forward(const dpo_bf16* hidden, const dpo_bf16* w, const int32
   f.hdr = at<WsHeader>(ws, L.hdr);
   f.part = at<float2>(ws, L.part);
   f.tgt_logit = at<float>(ws, L.tlogit);
+  f.part_z = op == DPO_OP_SEQ_LOGPS_METRICS ? at<float>(ws, L.partz) : nullptr;
   RUN("fwd_gemm", launch_fwd_gemm(f, persistent_grid(), st));
+  return DPO_OK;
+}
+
+int enqueue_fused_forward(const dpo_bf16* hidden, const dpo_bf16* w, const int32_t* targets,
+                          const uint8_t* mask, int rows, int T, int H, int V, float* sum32,
+                          double* sum64, float* lse, int32_t* n_tokens, void* ws, int op,
+                          hipStream_t st, double* logit_sum = nullptr) {
+  const Layout L = make_layout(op, rows, T, H, V);
+  FwdArgs f;
+  int rc = enqueue_forward_tiles(hidden, w, targets, mask, rows, T, H, V, lse, ws, op, st, {0, V},
+                                 OffMask(), f);
+  if (rc) return rc;
   CombineArgs c;
   c.part = f.part;
   c.tgt_logit = f.tgt_logit;
@@ -270,8 +312,37 @@ int enqueue_fused_forward(const dpo_bf16* hidden, const dpo_bf16* w, const int32
   r.sum64 = sum64;
   r.n_tokens = n_tokens;
   RUN("row_sums", launch_row_sums(r, st));
+  if (logit_sum) {
+    ZsumArgs z;
+    z.part_z = f.part_z;
+    z.hdr = f.hdr;
+    z.Mp = L.Mp;
+    z.nVt = L.nVt;
+    z.zsum64 = at<double>(ws, L.zsum64);
+    RUN("logit_sums", launch_zsum(z, st));
+    RowSumArgs q;
+    q.logp64 = z.zsum64;
+    q.row_off = r.row_off;
+    q.hdr = f.hdr;
+    q.rows = rows;
+    q.sum32 = nullptr;
+    q.sum64 = logit_sum;
+    q.n_tokens = nullptr;
+    RUN("logit_row_sums", launch_row_sums(q, st));
+  }
   return DPO_OK;
 }
+
+int check_slice(int V_shard, int v_begin, int V_total) {
+  if (v_begin < 0 || V_total <= 0 || V_total >= (1 << 30) || (long long)v_begin + V_shard > V_total)
+    return DPO_ERR_SHAPE;
+  return DPO_OK;
+}
+
+int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t* targets,
+                          const uint8_t* mask, int rows, int T, int H, int V, VocabSlice vs,
+                          const float* lse, const float* weight, float* d_hidden, float* d_w_vocab,
+                          int accumulate_dw, void* workspace, hipStream_t st);
 
 }  // namespace
 
@@ -281,8 +352,8 @@ int enqueue_fused_forward(const dpo_bf16* hidden, const dpo_bf16* w, const int32
 extern "C" {
 
 size_t dpo_workspace_bytes(int op, int rows, int T, int H, int V) {
-  if (op < DPO_OP_SEQ_LOGPS || op > DPO_OP_LOGITS_BACKWARD) return 0;
-  const bool need_h = op <= DPO_OP_HEAD_BACKWARD;
+  if (!op_known(op)) return 0;
+  const bool need_h = op_needs_h(op);
   if (!shape_ok(rows, T, H, V, need_h)) return 0;
   return make_layout(op, rows, T, need_h ? H : 0, V).total;
 }
@@ -312,19 +383,137 @@ int dpo_ref_score(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t
                                nullptr, nullptr, workspace, DPO_OP_REF_SCORE, (hipStream_t)stream);
 }
 
-int dpo_loss(const double* policy_sum64, const float* ref_sum, int num_pairs, double beta, int layout,
-             float* loss, float* weight, float* reward, float* margin, float* accuracy, void* stream) {
-  if (!policy_sum64 || !ref_sum || !loss || !weight) return DPO_ERR_NULL;
+int dpo_seq_logps_metrics(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t* targets,
+                          const uint8_t* mask, int rows, int T, int H, int V, float* logp_sum,
+                          double* logp_sum64, float* lse, int32_t* n_tokens, double* logit_sum,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!hidden || !w_vocab || !logp_sum || !logit_sum) return DPO_ERR_NULL;
+  int rc = check_common(targets, mask, rows, T, H, V, true, DPO_OP_SEQ_LOGPS_METRICS, workspace_bytes,
+                        workspace);
+  if (rc) return rc;
+  if (!aligned16(hidden) || !aligned16(w_vocab) || !aligned16(logp_sum) || !aligned16(logit_sum) ||
+      (logp_sum64 && !aligned16(logp_sum64)) || (lse && !aligned16(lse)))
+    return DPO_ERR_ALIGN;
+  return enqueue_fused_forward(hidden, w_vocab, targets, mask, rows, T, H, V, logp_sum, logp_sum64,
+                               lse, n_tokens, workspace, DPO_OP_SEQ_LOGPS_METRICS, (hipStream_t)stream,
+                               logit_sum);
+}
+
+int dpo_logits_mean(const double* logit_sum, const int32_t* n_tokens, int num_pairs, int V, int layout,
+                    float* means, void* stream) {
+  if (!logit_sum || !n_tokens || !means) return DPO_ERR_NULL;
+  if (num_pairs <= 0 || num_pairs >= (1 << 29) || V <= 0) return DPO_ERR_SHAPE;
+  if (layout != DPO_PAIRS_ADJACENT && layout != DPO_PAIRS_HALVES) return DPO_ERR_LAYOUT;
+  hipStream_t st = (hipStream_t)stream;
+  LogitsMeanArgs a{logit_sum, n_tokens, num_pairs, layout, V, means};
+  RUN("logits_mean", launch_logits_mean(a, st));
+  return DPO_OK;
+}
+
+int dpo_seq_logps_shard(const dpo_bf16* hidden, const dpo_bf16* w_shard, const int32_t* targets,
+                        const uint8_t* mask, int rows, int T, int H, int V_shard, int v_begin, int V_total,
+                        float* part_max, float* part_sumexp, float* part_tgt, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!hidden || !w_shard || !part_max || !part_sumexp || !part_tgt) return DPO_ERR_NULL;
+  int rc = check_common(targets, mask, rows, T, H, V_shard, true, DPO_OP_SEQ_LOGPS, workspace_bytes,
+                        workspace);
+  if (rc) return rc;
+  rc = check_slice(V_shard, v_begin, V_total);
+  if (rc) return rc;
+  if (!aligned16(hidden) || !aligned16(w_shard) || !aligned16(part_max) || !aligned16(part_sumexp) ||
+      !aligned16(part_tgt))
+    return DPO_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const Layout L = make_layout(DPO_OP_SEQ_LOGPS, rows, T, H, V_shard);
+  OffMask off;
+  off.max = part_max;
+  off.sum = part_sumexp;
+  off.tgt = part_tgt;
+  FwdArgs f;
+  rc = enqueue_forward_tiles(hidden, w_shard, targets, mask, rows, T, H, V_shard, nullptr, workspace,
+                             DPO_OP_SEQ_LOGPS, st, {v_begin, V_total}, off, f);
+  if (rc) return rc;
+  ShardPartialArgs p;
+  p.part = f.part;
+  p.tgt_logit = f.tgt_logit;
+  p.tgt_c = f.tgt_c;
+  p.idx = f.idx;
+  p.hdr = f.hdr;
+  p.Mp = L.Mp;
+  p.nVt = L.nVt;
+  p.out_max = part_max;
+  p.out_sum = part_sumexp;
+  p.out_tgt = part_tgt;
+  RUN("shard_partials", launch_shard_partials(p, L.Mp, st));
+  return DPO_OK;
+}
+
+int dpo_shard_combine(const float* part_max, const float* part_sumexp, const float* part_tgt,
+                      int num_shards, const int32_t* targets, const uint8_t* mask, int rows, int T,
+                      int V_total, float* logp_sum, double* logp_sum64, float* lse, int32_t* n_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!part_max || !part_sumexp || !part_tgt || !logp_sum) return DPO_ERR_NULL;
+  int rc = check_common(targets, mask, rows, T, 0, V_total, false, DPO_OP_SHARD_COMBINE, workspace_bytes,
+                        workspace);
+  if (rc) return rc;
+  if (num_shards <= 0 || num_shards > 4096 || (long long)num_shards * rows * T >= (1LL << 40))
+    return DPO_ERR_SHAPE;
+  if (!aligned16(part_max) || !aligned16(part_sumexp) || !aligned16(part_tgt) || !aligned16(logp_sum) ||
+      (logp_sum64 && !aligned16(logp_sum64)) || (lse && !aligned16(lse)))
+    return DPO_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const Layout L = make_layout(DPO_OP_SHARD_COMBINE, rows, T, 0, V_total);
+  rc = enqueue_compact(L, workspace, targets, mask, rows, T, V_total, lse, st);
+  if (rc) return rc;
+  ShardCombineArgs c;
+  c.pmax = part_max;
+  c.psum = part_sumexp;
+  c.ptgt = part_tgt;
+  c.S = num_shards;
+  c.stride = (long)rows * T;
+  c.idx = at<int>(workspace, L.idx);
+  c.tgt_c = at<int>(workspace, L.tgt);
+  c.hdr = at<WsHeader>(workspace, L.hdr);
+  c.lse64 = at<double>(workspace, L.lse64);
+  c.logp64 = at<double>(workspace, L.logp64);
+  c.lse_out = lse;
+  RUN("shard_combine", launch_shard_combine(c, L.Mp, st));
+  RowSumArgs r;
+  r.logp64 = c.logp64;
+  r.row_off = at<int>(workspace, L.rowoff);
+  r.hdr = c.hdr;
+  r.rows = rows;
+  r.sum32 = logp_sum;
+  r.sum64 = logp_sum64;
+  r.n_tokens = n_tokens;
+  RUN("row_sums", launch_row_sums(r, st));
+  return DPO_OK;
+}
+
+int dpo_loss_ex(const double* policy_sum64, const float* ref_sum, const int32_t* n_tokens, int num_pairs,
+                double beta, int layout, int flags, double sft_alpha, float* loss, float* weight,
+                float* reward, float* margin, float* accuracy, float* nll, void* stream) {
+  if (!policy_sum64 || !loss || !weight) return DPO_ERR_NULL;
+  if (flags & ~(DPO_LOSS_LENGTH_NORM | DPO_LOSS_REFERENCE_FREE)) return DPO_ERR_LAYOUT;
+  const bool ref_free = (flags & DPO_LOSS_REFERENCE_FREE) != 0;
+  const bool length_norm = (flags & DPO_LOSS_LENGTH_NORM) != 0;
+  if (!ref_free && !ref_sum) return DPO_ERR_NULL;
+  if (!(isfinite(sft_alpha) && sft_alpha >= 0.0)) return DPO_ERR_ALPHA;
+  if ((length_norm || sft_alpha > 0.0 || nll) && !n_tokens) return DPO_ERR_NULL;
   if (num_pairs <= 0 || num_pairs >= (1 << 29)) return DPO_ERR_SHAPE;
   if (!(isfinite(beta) && beta > 0.0)) return DPO_ERR_BETA;
   if (layout != DPO_PAIRS_ADJACENT && layout != DPO_PAIRS_HALVES) return DPO_ERR_LAYOUT;
   hipStream_t st = (hipStream_t)stream;
   LossArgs a;
   a.policy = policy_sum64;
-  a.ref = ref_sum;
+  a.ref = ref_free ? nullptr : ref_sum;
+  a.n_tokens = (length_norm || sft_alpha > 0.0 || nll) ? n_tokens : nullptr;
   a.num_pairs = num_pairs;
   a.layout = layout;
+  a.length_norm = length_norm ? 1 : 0;
   a.beta = beta;
+  a.alpha = sft_alpha;
+  a.nll = nll;
   a.loss = loss;
   a.weight = weight;
   a.reward = reward;
@@ -332,6 +521,13 @@ int dpo_loss(const double* policy_sum64, const float* ref_sum, int num_pairs, do
   a.accuracy = accuracy;
   RUN("loss", launch_loss(a, st));
   return DPO_OK;
+}
+
+int dpo_loss(const double* policy_sum64, const float* ref_sum, int num_pairs, double beta, int layout,
+             float* loss, float* weight, float* reward, float* margin, float* accuracy, void* stream) {
+  if (!policy_sum64 || !ref_sum || !loss || !weight) return DPO_ERR_NULL;
+  return dpo_loss_ex(policy_sum64, ref_sum, nullptr, num_pairs, beta, layout, 0, 0.0, loss, weight, reward,
+                     margin, accuracy, nullptr, stream);
 }
 
 int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t* targets,
@@ -346,10 +542,40 @@ int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int
   if (!aligned16(hidden) || !aligned16(w_vocab) || !aligned16(lse) || !aligned16(d_hidden) ||
       !aligned16(d_w_vocab))
     return DPO_ERR_ALIGN;
-  hipStream_t st = (hipStream_t)stream;
+  return enqueue_head_backward(hidden, w_vocab, targets, mask, rows, T, H, V, {0, V}, lse, weight,
+                               d_hidden, d_w_vocab, accumulate_dw, workspace, (hipStream_t)stream);
+}
+
+int dpo_head_backward_shard(const dpo_bf16* hidden, const dpo_bf16* w_shard, const int32_t* targets,
+                            const uint8_t* mask, int rows, int T, int H, int V_shard, int v_begin,
+                            int V_total, const float* lse, const float* weight, float* d_hidden,
+                            float* d_w_shard, int accumulate_dw, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!hidden || !w_shard || !lse || !weight || !d_hidden || !d_w_shard) return DPO_ERR_NULL;
+  int rc = check_common(targets, mask, rows, T, H, V_shard, true, DPO_OP_HEAD_BACKWARD, workspace_bytes,
+                        workspace);
+  if (rc) return rc;
+  rc = check_slice(V_shard, v_begin, V_total);
+  if (rc) return rc;
+  if (accumulate_dw != 0 && accumulate_dw != 1) return DPO_ERR_LAYOUT;
+  if (!aligned16(hidden) || !aligned16(w_shard) || !aligned16(lse) || !aligned16(d_hidden) ||
+      !aligned16(d_w_shard))
+    return DPO_ERR_ALIGN;
+  return enqueue_head_backward(hidden, w_shard, targets, mask, rows, T, H, V_shard, {v_begin, V_total},
+                               lse, weight, d_hidden, d_w_shard, accumulate_dw, workspace,
+                               (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t* targets,
+                          const uint8_t* mask, int rows, int T, int H, int V, VocabSlice vs,
+                          const float* lse, const float* weight, float* d_hidden, float* d_w_vocab,
+                          int accumulate_dw, void* workspace, hipStream_t st) {
   const Layout L = make_layout(DPO_OP_HEAD_BACKWARD, rows, T, H, V);
   void* ws = workspace;
-  rc = enqueue_compact(L, ws, targets, mask, rows, T, V, nullptr, st);
+  int rc = enqueue_compact(L, ws, targets, mask, rows, T, V, nullptr, st, vs);
   if (rc) return rc;
   WsHeader* hdr = at<WsHeader>(ws, L.hdr);
   uint16_t* D = at<uint16_t>(ws, L.D);
@@ -424,14 +650,16 @@ int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int
   RUN("dw_gemm", launch_dw_gemm(dw, persistent_grid(), st));
 
   // one-hot term of dW_vocab: sort positions by target, subtract per-target sums
+  // (keys span [0, V], V standing for "no target in this slice")
   int bits = 1;
-  while (bits < 31 && (1 << bits) < V) ++bits;
+  while (bits < 31 && (1 << bits) <= V) ++bits;
   SortArgs so;
   so.tgt_c = dp.tgt_c;
   so.idx = dp.idx;
   so.row_c = dp.row_c;
   so.weight = weight;
   so.hdr = hdr;
+  so.V = V;
   so.passes = (bits + 7) / 8;
   so.keysA = at<int>(ws, L.keysA);
   so.valsA = at<int>(ws, L.valsA);
@@ -454,10 +682,16 @@ int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int
   RUN("onehot_dw", launch_onehot_dw(oh, L.Mp, st));
   return DPO_OK;
 }
+}  // namespace
 
-int dpo_logits_seq_logps(const dpo_bf16* logits, const int32_t* targets, const uint8_t* mask, int rows,
-                         int T, int V, float* logp_sum, double* logp_sum64, float* lse,
-                         int32_t* n_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" {
+
+}  // extern "C"
+
+namespace {
+int logits_forward(const void* logits, bool f32, const int32_t* targets, const uint8_t* mask, int rows,
+                   int T, int V, float* logp_sum, double* logp_sum64, float* lse, int32_t* n_tokens,
+                   void* workspace, size_t workspace_bytes, void* stream) {
   if (!logits || !logp_sum) return DPO_ERR_NULL;
   int rc = check_common(targets, mask, rows, T, 0, V, false, DPO_OP_LOGITS_SEQ_LOGPS, workspace_bytes,
                         workspace);
@@ -479,7 +713,10 @@ int dpo_logits_seq_logps(const dpo_bf16* logits, const int32_t* targets, const u
   f.lse64 = at<double>(ws, L.lse64);
   f.logp64 = at<double>(ws, L.logp64);
   f.lse_out = lse;
-  RUN("stream_fwd", launch_stream_fwd(f, (long)rows * T, st));
+  if (f32)
+    RUN("stream_fwd_f32", launch_stream_fwd_f32(f, (long)rows * T, st));
+  else
+    RUN("stream_fwd", launch_stream_fwd(f, (long)rows * T, st));
   RowSumArgs r;
   r.logp64 = f.logp64;
   r.row_off = at<int>(ws, L.rowoff);
@@ -492,9 +729,9 @@ int dpo_logits_seq_logps(const dpo_bf16* logits, const int32_t* targets, const u
   return DPO_OK;
 }
 
-int dpo_logits_backward(const dpo_bf16* logits, const int32_t* targets, const uint8_t* mask, int rows,
-                        int T, int V, const float* lse, const float* weight, dpo_bf16* d_logits,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+int logits_backward(const void* logits, bool f32, const int32_t* targets, const uint8_t* mask, int rows,
+                    int T, int V, const float* lse, const float* weight, void* d_logits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   if (!logits || !lse || !weight || !d_logits) return DPO_ERR_NULL;
   int rc = check_common(targets, mask, rows, T, 0, V, false, DPO_OP_LOGITS_BACKWARD, workspace_bytes,
                         workspace);
@@ -514,8 +751,42 @@ int dpo_logits_backward(const dpo_bf16* logits, const int32_t* targets, const ui
   b.weight = weight;
   b.hdr = hdr;
   b.d_logits = d_logits;
-  RUN("stream_bwd", launch_stream_bwd(b, (long)rows * T, st));
+  if (f32)
+    RUN("stream_bwd_f32", launch_stream_bwd_f32(b, (long)rows * T, st));
+  else
+    RUN("stream_bwd", launch_stream_bwd(b, (long)rows * T, st));
   return DPO_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int dpo_logits_seq_logps(const dpo_bf16* logits, const int32_t* targets, const uint8_t* mask, int rows,
+                         int T, int V, float* logp_sum, double* logp_sum64, float* lse,
+                         int32_t* n_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  return logits_forward(logits, false, targets, mask, rows, T, V, logp_sum, logp_sum64, lse, n_tokens,
+                        workspace, workspace_bytes, stream);
+}
+
+int dpo_logits_backward(const dpo_bf16* logits, const int32_t* targets, const uint8_t* mask, int rows,
+                        int T, int V, const float* lse, const float* weight, dpo_bf16* d_logits,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return logits_backward(logits, false, targets, mask, rows, T, V, lse, weight, d_logits, workspace,
+                         workspace_bytes, stream);
+}
+
+int dpo_logits_f32_seq_logps(const float* logits, const int32_t* targets, const uint8_t* mask, int rows,
+                             int T, int V, float* logp_sum, double* logp_sum64, float* lse,
+                             int32_t* n_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  return logits_forward(logits, true, targets, mask, rows, T, V, logp_sum, logp_sum64, lse, n_tokens,
+                        workspace, workspace_bytes, stream);
+}
+
+int dpo_logits_f32_backward(const float* logits, const int32_t* targets, const uint8_t* mask, int rows,
+                            int T, int V, const float* lse, const float* weight, float* d_logits,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return logits_backward(logits, true, targets, mask, rows, T, V, lse, weight, d_logits, workspace,
+                         workspace_bytes, stream);
 }
 
 int dpo_device_status(void* workspace, void* stream) {
@@ -535,8 +806,10 @@ const char* dpo_strerror(int status) {
     case DPO_ERR_BETA: return "beta must be finite and > 0";
     case DPO_ERR_LAYOUT: return "unknown pair layout or flag value";
     case DPO_ERR_WORKSPACE: return "workspace smaller than dpo_workspace_bytes()";
-    case DPO_ERR_TARGET_RANGE: return "a target id at a completion position is outside [0, V)";
+    case DPO_ERR_TARGET_RANGE:
+      return "a target id at a completion position is outside [0, V) (or no vocabulary shard holds it)";
     case DPO_ERR_HIP: return "a HIP runtime call failed";
+    case DPO_ERR_ALPHA: return "sft_alpha must be finite and >= 0";
     default: return "unknown status";
   }
 }

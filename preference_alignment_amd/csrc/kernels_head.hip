@@ -70,16 +70,24 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CompactArgs a) {
     if (p % a.T == 0) a.row_off[p / a.T] = pos;
     if (a.mask[p] != 0) {
       int t = a.targets[p];
-      if (t < 0 || t >= a.V) {
+      if (t < 0 || t >= a.V_total) {
         bad = 1;
         t = -1;
+      } else {
+        t -= a.v_begin;
+        if (t < 0 || t >= a.V) t = -1;  // held by another vocabulary shard
       }
       a.idx[pos] = (int)p;
       a.tgt_c[pos] = t;
       a.row_c[pos] = (int)(p / a.T);
       ++pos;
-    } else if (a.lse_out) {
-      a.lse_out[p] = 0.f;
+    } else {
+      if (a.lse_out) a.lse_out[p] = 0.f;
+      if (a.off_max) {
+        a.off_max[p] = -INFINITY;
+        a.off_sum[p] = 0.f;
+        a.off_tgt[p] = -INFINITY;
+      }
     }
   }
   if (bad) atomicOr(&err, kStatusTargetRange);
@@ -118,10 +126,12 @@ __device__ __forceinline__ void for_vocab(const Acc& acc, int j, bool full, int 
     }
 }
 
+template <bool ZSUM>
 __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int* tgt_s = (int*)(smem + PIPE_BYTES);                  // 256 ints
   float2* red = (float2*)(smem + PIPE_BYTES + 1024);       // [2][256]
+  float* red_z = (float*)(smem + PIPE_BYTES + 5120);       // [2][256] (logit sums)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -158,6 +168,12 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
       float s = 0.f;
       for_vocab(acc, j, full, vbase, a.V, lane, [&](float v) { s += fast_exp2(fmaf(v, kLog2e, -ml)); });
       s += __shfl_xor(s, 32, 64);
+      if (ZSUM) {
+        float zs = 0.f;
+        for_vocab(acc, j, full, vbase, a.V, lane, [&](float v) { zs += v; });
+        zs += __shfl_xor(zs, 32, 64);
+        if (lane < 32) red_z[wm * 256 + pl] = zs;
+      }
       const int off = tgt_s[pl] - vbase;
       if (off >= 0 && off < 128) {
         const int r = off & 31;
@@ -180,6 +196,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
       const float S = (p0.x == -INFINITY ? 0.f : p0.y * fast_exp2((p0.x - M) * kLog2e)) +
                       (p1.x == -INFINITY ? 0.f : p1.y * fast_exp2((p1.x - M) * kLog2e));
       if (m0 + tid < n_c) a.part[(size_t)nt * a.Mp + m0 + tid] = make_float2(M, S);
+      if (ZSUM && m0 + tid < n_c) a.part_z[(size_t)nt * a.Mp + m0 + tid] = red_z[tid] + red_z[256 + tid];
     }
     __syncthreads();
   }
@@ -256,6 +273,58 @@ __global__ __launch_bounds__(256) void k_row_sums(RowSumArgs a) {
     if (a.sum64) a.sum64[r] = v;
     if (a.n_tokens) a.n_tokens[r] = hi - lo;
   }
+}
+
+// per position: the sum of its V logits from the per-tile sums, fp64, tiles in order
+__global__ __launch_bounds__(256) void k_zsum(ZsumArgs a) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= a.hdr->n_c) return;
+  double z = 0.0;
+  for (int j = 0; j < a.nVt; ++j) z += (double)a.part_z[(size_t)j * a.Mp + m];
+  a.zsum64[m] = z;
+}
+
+// ---------------------------------------------------------------------------
+// vocabulary shards: a shard's (max, sum exp, target logit) per position, and
+// the combine of S shards' values into the whole-vocabulary lse and log p
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_shard_partials(ShardPartialArgs a) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= a.hdr->n_c) return;
+  float M = -INFINITY;
+  for (int j = 0; j < a.nVt; ++j) M = fmaxf(M, a.part[(size_t)j * a.Mp + m].x);
+  double S = 0.0;
+  const float Ml = M * kLog2e;
+  for (int j = 0; j < a.nVt; ++j) {
+    const float2 t = a.part[(size_t)j * a.Mp + m];
+    S += (double)(t.y * fast_exp2(fmaf(t.x, kLog2e, -Ml)));
+  }
+  const int p = a.idx[m];
+  a.out_max[p] = M;
+  a.out_sum[p] = (float)S;
+  a.out_tgt[p] = a.tgt_c[m] >= 0 ? a.tgt_logit[m] : -INFINITY;
+}
+
+__global__ __launch_bounds__(256) void k_shard_combine(ShardCombineArgs a) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= a.hdr->n_c) return;
+  const size_t p = (size_t)a.idx[m];
+  float M = -INFINITY, tg = -INFINITY;
+  for (int q = 0; q < a.S; ++q) {
+    M = fmaxf(M, a.pmax[q * a.stride + p]);
+    tg = fmaxf(tg, a.ptgt[q * a.stride + p]);
+  }
+  double S = 0.0;
+  for (int q = 0; q < a.S; ++q) {
+    const float mq = a.pmax[q * a.stride + p];
+    if (mq != -INFINITY) S += (double)a.psum[q * a.stride + p] * exp((double)mq - (double)M);
+  }
+  const double lse = (double)M + log(S);
+  const bool ok = a.tgt_c[m] >= 0 && tg != -INFINITY;
+  if (!ok) atomicOr(&a.hdr->status, kStatusTargetRange);
+  a.lse64[m] = lse;
+  a.logp64[m] = ok ? (double)tg - lse : __builtin_nan("");
+  if (a.lse_out) a.lse_out[p] = (float)lse;
 }
 
 // ---------------------------------------------------------------------------
@@ -538,6 +607,13 @@ __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
 // entry gets its flat position and row weight, for k_onehot_dw.
 constexpr int kSortWaves = kSortThreads / 64;
 
+// the first pass reads the raw targets: ids outside [0, V) (out of range, or
+// held by another vocabulary shard) become V, so they sort after every valid id
+__device__ __forceinline__ int sort_key(const int* kin, int i, int pass, int V) {
+  const int k = kin[i];
+  return (pass > 0 || ((unsigned)k < (unsigned)V)) ? k : V;
+}
+
 __global__ __launch_bounds__(kSortThreads) void k_sort_targets(SortArgs a) {
   __shared__ int cnt[kSortWaves][256];
   __shared__ int dig_base[256];
@@ -558,7 +634,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_targets(SortArgs a) {
     __syncthreads();
     for (int base = lo; base < hi; base += 64) {
       const int i = base + lane;
-      if (i < hi) atomicAdd(&cnt[wave][((unsigned)kin[i] >> shift) & 255u], 1);
+      if (i < hi) atomicAdd(&cnt[wave][((unsigned)sort_key(kin, i, p, a.V) >> shift) & 255u], 1);
     }
     __syncthreads();
     if (tid < 256) {
@@ -583,7 +659,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_targets(SortArgs a) {
     for (int base = lo; base < hi; base += 64) {
       const int i = base + lane;
       const bool valid = i < hi;
-      const int k = valid ? kin[i] : 0;
+      const int k = valid ? sort_key(kin, i, p, a.V) : 0;
       const int d = ((unsigned)k >> shift) & 255u;
       const unsigned long long vmask = __ballot(valid);
       unsigned long long peers = vmask;
@@ -741,9 +817,29 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fwd_gemm(const FwdArgs& a, int grid, hipStream_t s) {
-  static hipError_t once = prep_gemm((const void*)k_fwd_gemm);
+  static hipError_t once = prep_gemm((const void*)k_fwd_gemm<false>);
+  static hipError_t once_z = prep_gemm((const void*)k_fwd_gemm<true>);
   if (once != hipSuccess) return once;
-  hipLaunchKernelGGL(k_fwd_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+  if (once_z != hipSuccess) return once_z;
+  if (a.part_z)
+    hipLaunchKernelGGL(k_fwd_gemm<true>, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+  else
+    hipLaunchKernelGGL(k_fwd_gemm<false>, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zsum(const ZsumArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_zsum, dim3(a.Mp / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_partials(const ShardPartialArgs& a, int Mp, hipStream_t s) {
+  hipLaunchKernelGGL(k_shard_partials, dim3(Mp / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_combine(const ShardCombineArgs& a, int Mp, hipStream_t s) {
+  hipLaunchKernelGGL(k_shard_combine, dim3(Mp / 256), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

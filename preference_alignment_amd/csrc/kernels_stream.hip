@@ -1,4 +1,4 @@
-// Bandwidth-bound variant over pre-materialised bf16 logits, and the loss.
+// Bandwidth-bound variant over pre-materialised logits, and the loss.
 //
 // Same method as the fused path ("DPO Training on GPU, in depth", sections
 // "What one DPO step computes" and "A training configuration that fits"), for
@@ -11,7 +11,11 @@
 //   k_stream_bwd   one workgroup per position: dlogits = w (exp(x - lse) - onehot)
 //                  rounded to bf16, exactly zero at positions outside the mask
 //   k_loss         the sigmoid DPO loss, its per-row gradient weights, rewards,
-//                  margins and accuracy, in fp64 ("A worked example of the numbers")
+//                  margins and accuracy, in fp64 ("A worked example of the numbers"),
+//                  with the reference-free, length-normalised and NLL-term variants
+//   k_logits_mean  mean chosen / rejected logit from the forward's logit sums
+// The streaming kernels take bf16 or fp32 logits (the page's memory section
+// sizes fp32 logits of one 2,048-token sequence at 0.98 GiB).
 #include "dpo_common.h"
 #include "launch.h"
 
@@ -30,14 +34,55 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = M;
 }
 
-__device__ __forceinline__ void absorb8(float& m, float& s, const u32x4 v) {
-  float x[8];
+// Element types of the logits: 16-byte vectors hold 8 bf16 or 4 fp32 values.
+template <typename E>
+struct Elem;
+template <>
+struct Elem<uint16_t> {
+  static constexpr int kPerVec = 8;
+  static __device__ __forceinline__ void unpack(const u32x4 v, float* x) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    x[2 * k] = bf16_lo(v[k]);
-    x[2 * k + 1] = bf16_hi(v[k]);
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = bf16_lo(v[k]);
+      x[2 * k + 1] = bf16_hi(v[k]);
+    }
   }
-  float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  static __device__ __forceinline__ u32x4 pack(const float* d) {  // round to nearest even
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(d[2 * k], d[2 * k + 1]);
+    return o;
+  }
+  static __device__ __forceinline__ float scalar(const void* base, size_t i) {
+    return bf16_bits_to_float(((const uint16_t*)base)[i]);
+  }
+};
+template <>
+struct Elem<float> {
+  static constexpr int kPerVec = 4;
+  static __device__ __forceinline__ void unpack(const u32x4 v, float* x) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(v[k]);
+  }
+  static __device__ __forceinline__ u32x4 pack(const float* d) {
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = __float_as_uint(d[k]);
+    return o;
+  }
+  static __device__ __forceinline__ float scalar(const void* base, size_t i) {
+    return ((const float*)base)[i];
+  }
+};
+
+template <typename E>
+__device__ __forceinline__ void absorb(float& m, float& s, const u32x4 v) {
+  constexpr int N = Elem<E>::kPerVec;
+  float x[N];
+  Elem<E>::unpack(v, x);
+  float lm = x[0];
+#pragma unroll
+  for (int k = 1; k < N; ++k) lm = fmaxf(lm, x[k]);
   if (lm > m) {
     s *= fast_exp2((m - lm) * kLog2e);
     m = lm;
@@ -45,18 +90,19 @@ __device__ __forceinline__ void absorb8(float& m, float& s, const u32x4 v) {
   const float ml = m * kLog2e;
   float acc = 0.f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) acc += fast_exp2(fmaf(x[k], kLog2e, -ml));
+  for (int k = 0; k < N; ++k) acc += fast_exp2(fmaf(x[k], kLog2e, -ml));
   s += acc;
 }
 
+template <typename E>
 __global__ __launch_bounds__(kStreamThreads) void k_stream_fwd(StreamFwdArgs a) {
   __shared__ float2 red[kStreamThreads / 64];
   const int m = blockIdx.x;
   if (m >= a.hdr->n_c) return;
   const int tid = threadIdx.x;
   const size_t pos = (size_t)a.idx[m];
-  const u32x4* row = (const u32x4*)(a.logits + pos * a.V);
-  const int nvec = a.V / 8;
+  const u32x4* row = (const u32x4*)((const E*)a.logits + pos * a.V);
+  const int nvec = a.V / Elem<E>::kPerVec;
   float mx = -INFINITY, s = 0.f;
   int v = tid;
   for (; v + (kStreamUnroll - 1) * kStreamThreads < nvec; v += kStreamUnroll * kStreamThreads) {
@@ -64,9 +110,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_fwd(StreamFwdArgs a) 
 #pragma unroll
     for (int u = 0; u < kStreamUnroll; ++u) buf[u] = __builtin_nontemporal_load(row + v + u * kStreamThreads);
 #pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) absorb8(mx, s, buf[u]);
+    for (int u = 0; u < kStreamUnroll; ++u) absorb<E>(mx, s, buf[u]);
   }
-  for (; v < nvec; v += kStreamThreads) absorb8(mx, s, __builtin_nontemporal_load(row + v));
+  for (; v < nvec; v += kStreamThreads) absorb<E>(mx, s, __builtin_nontemporal_load(row + v));
   // fixed-order combine: wave butterflies, then the 4 waves in order
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -82,18 +128,20 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_fwd(StreamFwdArgs a) 
     const double lse = (double)M + log((double)S);
     const int t = a.tgt_c[m];
     a.lse64[m] = lse;
-    a.logp64[m] = t >= 0 ? (double)bf16_bits_to_float(a.logits[pos * a.V + t]) - lse : __builtin_nan("");
+    a.logp64[m] = t >= 0 ? (double)Elem<E>::scalar(a.logits, pos * a.V + t) - lse : __builtin_nan("");
     if (a.lse_out) a.lse_out[pos] = (float)lse;
   }
 }
 
 constexpr int kBwdUnroll = 8;
 
+template <typename E>
 __global__ __launch_bounds__(kStreamThreads) void k_stream_bwd(StreamBwdArgs a) {
+  constexpr int N = Elem<E>::kPerVec;
   const size_t p = blockIdx.x;
   const int tid = threadIdx.x;
-  const int nvec = a.V / 8;
-  u32x4* out = (u32x4*)(a.d_logits + p * a.V);
+  const int nvec = a.V / N;
+  u32x4* out = (u32x4*)((E*)a.d_logits + p * a.V);
   if (a.mask[p] == 0) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int v = tid; v < nvec; v += kStreamThreads) __builtin_nontemporal_store(z, out + v);
@@ -106,8 +154,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_bwd(StreamBwdArgs a) 
   }
   const float L = a.lse[p] * kLog2e;
   const float w = a.weight[p / a.T];
-  const int tv = tg >= 0 ? tg >> 3 : -1;  // the one vector holding the target
-  const u32x4* row = (const u32x4*)(a.logits + p * a.V);
+  const int tv = tg >= 0 ? tg / N : -1;  // the one vector holding the target
+  const u32x4* row = (const u32x4*)((const E*)a.logits + p * a.V);
   for (int v0 = tid; v0 < nvec; v0 += kBwdUnroll * kStreamThreads) {
     u32x4 buf[kBwdUnroll];
 #pragma unroll
@@ -119,20 +167,15 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_bwd(StreamBwdArgs a) 
     for (int u = 0; u < kBwdUnroll; ++u) {
       const int v = v0 + u * kStreamThreads;
       if (v >= nvec) break;
-      float d[8];
+      float x[N], d[N];
+      Elem<E>::unpack(buf[u], x);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        d[2 * k] = w * fast_exp2(fmaf(bf16_lo(buf[u][k]), kLog2e, -L));
-        d[2 * k + 1] = w * fast_exp2(fmaf(bf16_hi(buf[u][k]), kLog2e, -L));
-      }
+      for (int k = 0; k < N; ++k) d[k] = w * fast_exp2(fmaf(x[k], kLog2e, -L));
       if (v == tv) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) d[k] = (k == (tg & 7)) ? d[k] - w : d[k];
+        for (int k = 0; k < N; ++k) d[k] = (k == tg % N) ? d[k] - w : d[k];
       }
-      u32x4 o;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(d[2 * k], d[2 * k + 1]);
-      __builtin_nontemporal_store(o, out + v);
+      __builtin_nontemporal_store(Elem<E>::pack(d), out + v);
     }
   }
 }
@@ -148,24 +191,64 @@ __device__ __forceinline__ double sigmoid_d(double x) {
   return x >= 0 ? 1.0 / (1.0 + e) : e / (1.0 + e);
 }
 
+// Variants on the same scores: a NULL reference means reference-free scores;
+// length_norm divides each row's policy and reference score by its completion
+// token count (a row without tokens averages to 0); alpha > 0 adds alpha
+// times the mean negative log-probability per chosen completion token of the
+// batch (-sum pi_chosen / sum n_chosen) to the loss.
 __global__ __launch_bounds__(256) void k_loss(LossArgs a) {
   __shared__ double red_l[256];
+  __shared__ long long red_n[256];
   __shared__ int red_c[256];
   const int tid = threadIdx.x;
   const int B = a.num_pairs;
+  auto chosen = [&](int i) { return a.layout == 0 ? 2 * i : i; };
+  auto rejected = [&](int i) { return a.layout == 0 ? 2 * i + 1 : B + i; };
+  // chosen-row totals for the NLL term, in a fixed order
+  double nll = 0.0, inv_nch = 0.0;
+  if (a.n_tokens) {
+    double ps = 0.0;
+    long long nc = 0;
+    for (int i = tid; i < B; i += 256) {
+      ps += a.policy[chosen(i)];
+      nc += a.n_tokens[chosen(i)];
+    }
+    red_l[tid] = ps;
+    red_n[tid] = nc;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (tid < o) {
+        red_l[tid] += red_l[tid + o];
+        red_n[tid] += red_n[tid + o];
+      }
+      __syncthreads();
+    }
+    if (red_n[0] > 0) {
+      nll = -red_l[0] / (double)red_n[0];
+      inv_nch = 1.0 / (double)red_n[0];
+    }
+    __syncthreads();
+  }
+  auto scale = [&](int r) {
+    if (!a.length_norm) return 1.0;
+    const int n = a.n_tokens[r];
+    return n > 0 ? 1.0 / (double)n : 0.0;
+  };
   double lsum = 0.0;
   int correct = 0;
   for (int i = tid; i < B; i += 256) {
-    const int rc = a.layout == 0 ? 2 * i : i;
-    const int rr = a.layout == 0 ? 2 * i + 1 : B + i;
-    const double reward_c = a.beta * (a.policy[rc] - (double)a.ref[rc]);
-    const double reward_r = a.beta * (a.policy[rr] - (double)a.ref[rr]);
+    const int rc = chosen(i), rr = rejected(i);
+    const double sc = scale(rc), sr = scale(rr);
+    const double ref_c = a.ref ? (double)a.ref[rc] : 0.0;
+    const double ref_r = a.ref ? (double)a.ref[rr] : 0.0;
+    const double reward_c = a.beta * (a.policy[rc] - ref_c) * sc;
+    const double reward_r = a.beta * (a.policy[rr] - ref_r) * sr;
     const double margin = reward_c - reward_r;
     lsum += softplus_d(-margin);
     correct += margin > 0.0;
     const double g = a.beta * sigmoid_d(-margin) / (double)B;
-    a.weight[rc] = (float)g;
-    a.weight[rr] = (float)(-g);
+    a.weight[rc] = (float)(g * sc + a.alpha * inv_nch);
+    a.weight[rr] = (float)(-g * sr);
     if (a.reward) {
       a.reward[rc] = (float)reward_c;
       a.reward[rr] = (float)reward_r;
@@ -183,18 +266,70 @@ __global__ __launch_bounds__(256) void k_loss(LossArgs a) {
     __syncthreads();
   }
   if (tid == 0) {
-    a.loss[0] = (float)(red_l[0] / (double)B);
+    a.loss[0] = (float)(red_l[0] / (double)B + a.alpha * nll);
     if (a.accuracy) a.accuracy[0] = (float)((double)red_c[0] / (double)B);
+    if (a.nll) a.nll[0] = (float)nll;
+  }
+}
+
+// mean logit over completion positions and vocabulary, chosen and rejected halves
+__global__ __launch_bounds__(256) void k_logits_mean(LogitsMeanArgs a) {
+  __shared__ double red_s[2][256];
+  __shared__ long long red_n[2][256];
+  const int tid = threadIdx.x;
+  const int B = a.num_pairs;
+  double s0 = 0.0, s1 = 0.0;
+  long long n0 = 0, n1 = 0;
+  for (int i = tid; i < B; i += 256) {
+    const int rc = a.layout == 0 ? 2 * i : i;
+    const int rr = a.layout == 0 ? 2 * i + 1 : B + i;
+    s0 += a.logit_sum[rc];
+    n0 += a.n_tokens[rc];
+    s1 += a.logit_sum[rr];
+    n1 += a.n_tokens[rr];
+  }
+  red_s[0][tid] = s0;
+  red_s[1][tid] = s1;
+  red_n[0][tid] = n0;
+  red_n[1][tid] = n1;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) {
+      for (int h = 0; h < 2; ++h) {
+        red_s[h][tid] += red_s[h][tid + o];
+        red_n[h][tid] += red_n[h][tid + o];
+      }
+    }
+    __syncthreads();
+  }
+  if (tid < 2) {
+    const long long n = red_n[tid][0];
+    a.means[tid] = n > 0 ? (float)(red_s[tid][0] / ((double)n * (double)a.V)) : 0.f;
   }
 }
 
 hipError_t launch_stream_fwd(const StreamFwdArgs& a, long positions, hipStream_t s) {
-  hipLaunchKernelGGL(k_stream_fwd, dim3((unsigned)positions), dim3(kStreamThreads), 0, s, a);
+  hipLaunchKernelGGL(k_stream_fwd<uint16_t>, dim3((unsigned)positions), dim3(kStreamThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, hipStream_t s) {
-  hipLaunchKernelGGL(k_stream_bwd, dim3((unsigned)positions), dim3(kStreamThreads), 0, s, a);
+  hipLaunchKernelGGL(k_stream_bwd<uint16_t>, dim3((unsigned)positions), dim3(kStreamThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_fwd_f32(const StreamFwdArgs& a, long positions, hipStream_t s) {
+  hipLaunchKernelGGL(k_stream_fwd<float>, dim3((unsigned)positions), dim3(kStreamThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_bwd_f32(const StreamBwdArgs& a, long positions, hipStream_t s) {
+  hipLaunchKernelGGL(k_stream_bwd<float>, dim3((unsigned)positions), dim3(kStreamThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_logits_mean(const LogitsMeanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_logits_mean, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -13,13 +13,20 @@ namespace dpo {
 struct CompactArgs {
   const uint8_t* mask;
   const int32_t* targets;
-  int rows, T, V, Mp;
+  int rows, T, Mp;
+  int V;         // vocabulary rows this call works on (a shard's size, or the whole V)
+  int v_begin;   // global id of its first row
+  int V_total;   // whole vocabulary: targets outside [0, V_total) are errors
   WsHeader* hdr;
   int* idx;      // [Mp] flat position r*T+t of each completion position
-  int* tgt_c;    // [Mp] its target (-1: padding or out of range)
+  int* tgt_c;    // [Mp] its target relative to v_begin (-1: padding, out of range,
+                 //      or held by another vocabulary shard)
   int* row_c;    // [Mp] its row
   int* row_off;  // [rows+1] first completion position of each row
   float* lse_out;  // [rows*T] nullable; zeroed at mask-0 positions
+  float* off_max;  // [rows*T] nullable; -inf at mask-0 positions (shard partials)
+  float* off_sum;  // [rows*T] nullable; 0 at mask-0 positions
+  float* off_tgt;  // [rows*T] nullable; -inf at mask-0 positions
 };
 
 struct FwdArgs {
@@ -32,6 +39,41 @@ struct FwdArgs {
   const WsHeader* hdr;
   float2* part;      // [nVt, Mp] per-tile (max, sum exp)
   float* tgt_logit;  // [Mp]
+  float* part_z;     // [nVt, Mp] per-tile sum of the logits, or NULL
+};
+
+struct ZsumArgs {
+  const float* part_z;  // [nVt, Mp]
+  const WsHeader* hdr;
+  int Mp, nVt;
+  double* zsum64;  // [Mp] per position: sum of its V logits
+};
+
+// one vocabulary shard's (max, sum exp, target logit) per position, [rows*T]
+struct ShardPartialArgs {
+  const float2* part;
+  const float* tgt_logit;
+  const int* tgt_c;
+  const int* idx;
+  const WsHeader* hdr;
+  int Mp, nVt;
+  float* out_max;
+  float* out_sum;
+  float* out_tgt;
+};
+
+struct ShardCombineArgs {
+  const float* pmax;  // [S, rows*T]
+  const float* psum;
+  const float* ptgt;
+  int S;
+  long stride;  // rows*T
+  const int* idx;
+  const int* tgt_c;
+  WsHeader* hdr;
+  double* lse64;
+  double* logp64;
+  float* lse_out;  // nullable
 };
 
 struct CombineArgs {
@@ -111,6 +153,7 @@ struct SortArgs {
   const int* row_c;
   const float* weight;  // [rows]
   const WsHeader* hdr;
+  int V;                // keys outside [0, V) sort last, as V
   int passes;           // 8-bit digits needed to cover V
   int* keysA;
   int* valsA;
@@ -146,8 +189,10 @@ struct ZeroRowsArgs {
   float* d_hidden;
 };
 
+// The streaming kernels are instantiated for bf16 (uint16_t bits) and fp32
+// logits; `logits` / `d_logits` point to that element type.
 struct StreamFwdArgs {
-  const uint16_t* logits;  // [rows*T, V]
+  const void* logits;  // [rows*T, V]
   int V;
   const int* idx;
   const int* tgt_c;
@@ -158,21 +203,25 @@ struct StreamFwdArgs {
 };
 
 struct StreamBwdArgs {
-  const uint16_t* logits;
+  const void* logits;
   const int32_t* targets;
   const uint8_t* mask;
   int T, V;
   const float* lse;     // [rows*T]
   const float* weight;  // [rows]
   WsHeader* hdr;
-  uint16_t* d_logits;   // [rows*T, V]
+  void* d_logits;       // [rows*T, V], the input's element type
 };
 
 struct LossArgs {
   const double* policy;  // [2B]
-  const float* ref;      // [2B]
+  const float* ref;      // [2B]; NULL: reference-free
+  const int32_t* n_tokens;  // [2B]; needed for length normalisation and the NLL term
   int num_pairs, layout;
+  int length_norm;       // divide row scores by their token counts
   double beta;
+  double alpha;          // weight of the NLL term on chosen rows (0: none)
+  float* nll;       // [1] nullable
   float* loss;      // [1]
   float* weight;    // [2B]
   float* reward;    // [2B] nullable
@@ -198,5 +247,18 @@ hipError_t launch_stream_fwd(const StreamFwdArgs& a, long positions, hipStream_t
 hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, hipStream_t s);
 hipError_t launch_reset_status(WsHeader* hdr, hipStream_t s);
 hipError_t launch_loss(const LossArgs& a, hipStream_t s);
+hipError_t launch_zsum(const ZsumArgs& a, hipStream_t s);
+hipError_t launch_shard_partials(const ShardPartialArgs& a, int Mp, hipStream_t s);
+hipError_t launch_shard_combine(const ShardCombineArgs& a, int Mp, hipStream_t s);
+hipError_t launch_stream_fwd_f32(const StreamFwdArgs& a, long positions, hipStream_t s);
+hipError_t launch_stream_bwd_f32(const StreamBwdArgs& a, long positions, hipStream_t s);
+
+struct LogitsMeanArgs {
+  const double* logit_sum;  // [2B]
+  const int32_t* n_tokens;  // [2B]
+  int num_pairs, layout, V;
+  float* means;  // [2]: chosen, rejected
+};
+hipError_t launch_logits_mean(const LogitsMeanArgs& a, hipStream_t s);
 
 }  // namespace dpo

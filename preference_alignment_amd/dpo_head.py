@@ -24,6 +24,7 @@ DPO_ERR_LAYOUT = -5
 DPO_ERR_WORKSPACE = -6
 DPO_ERR_TARGET_RANGE = -7
 DPO_ERR_HIP = -8
+DPO_ERR_ALPHA = -9
 
 DPO_PAIRS_ADJACENT = 0
 DPO_PAIRS_HALVES = 1
@@ -33,6 +34,11 @@ DPO_OP_REF_SCORE = 1
 DPO_OP_HEAD_BACKWARD = 2
 DPO_OP_LOGITS_SEQ_LOGPS = 3
 DPO_OP_LOGITS_BACKWARD = 4
+DPO_OP_SHARD_COMBINE = 5
+DPO_OP_SEQ_LOGPS_METRICS = 6
+
+DPO_LOSS_LENGTH_NORM = 1
+DPO_LOSS_REFERENCE_FREE = 2
 
 HEADER = os.path.join(_build.ROOT, "include", "dpo_head.h")
 
@@ -47,6 +53,16 @@ _SIGS = {
     "dpo_head_backward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "dpo_logits_seq_logps": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
     "dpo_logits_backward": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "dpo_loss_ex": (_I, [_P, _P, _P, _I, ctypes.c_double, _I, _I, ctypes.c_double, _P, _P, _P, _P, _P, _P,
+                         _P]),
+    "dpo_logits_f32_seq_logps": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
+    "dpo_logits_f32_backward": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "dpo_seq_logps_shard": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "dpo_shard_combine": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
+    "dpo_head_backward_shard": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _Z,
+                                     _P]),
+    "dpo_seq_logps_metrics": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "dpo_logits_mean": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "dpo_device_status": (_I, [_P, _P]),
     "dpo_strerror": (ctypes.c_char_p, [_I]),
     "dpo_profile_enable": (_I, [_I]),
@@ -98,7 +114,7 @@ def _check(status: int) -> None:
         return
     msg = lib().dpo_strerror(status).decode()
     if status in (DPO_ERR_NULL, DPO_ERR_SHAPE, DPO_ERR_ALIGN, DPO_ERR_BETA, DPO_ERR_LAYOUT,
-                  DPO_ERR_WORKSPACE):
+                  DPO_ERR_WORKSPACE, DPO_ERR_ALPHA):
         raise ValueError(f"{msg} (status {status})")
     raise DpoError(status, msg)
 
@@ -252,6 +268,161 @@ def dpo_logits_backward(logits, targets, mask, lse, weight, d_logits, workspace=
     _check(lib().dpo_logits_backward(_ptr(logits), _ptr(targets), _ptr(mask), rows, T, V, _ptr(lse),
                                      _ptr(weight), _ptr(d_logits), _ptr(workspace), workspace.numel(),
                                      _stream(stream, logits)))
+
+
+def dpo_loss_ex(policy_sum64, ref_sum, n_tokens, beta: float, layout: int, flags: int, sft_alpha: float,
+                loss, weight, reward=None, margin=None, accuracy=None, nll=None, stream=None) -> None:
+    import torch
+    R = policy_sum64.shape[0]
+    _need(policy_sum64, torch.float64, "policy_sum64")
+    if ref_sum is not None:
+        _need(ref_sum, torch.float32, "ref_sum", (R,))
+    if n_tokens is not None:
+        _need(n_tokens, torch.int32, "n_tokens", (R,))
+    _need(loss, torch.float32, "loss", (1,))
+    _need(weight, torch.float32, "weight", (R,))
+    for t, name, shape in ((reward, "reward", (R,)), (margin, "margin", (R // 2,)),
+                           (accuracy, "accuracy", (1,)), (nll, "nll", (1,))):
+        if t is not None:
+            _need(t, torch.float32, name, shape)
+    if R % 2:
+        raise ValueError("rows must be even")
+    _check(lib().dpo_loss_ex(_ptr(policy_sum64), _ptr(ref_sum), _ptr(n_tokens), R // 2, float(beta),
+                             int(layout), int(flags), float(sft_alpha), _ptr(loss), _ptr(weight),
+                             _ptr(reward), _ptr(margin), _ptr(accuracy), _ptr(nll),
+                             _stream(stream, policy_sum64)))
+
+
+def dpo_logits_f32_seq_logps(logits, targets, mask, logp_sum, logp_sum64=None, lse=None, n_tokens=None,
+                             workspace=None, stream=None) -> None:
+    import torch
+    rows, T, V = logits.shape
+    _need(logits, torch.float32, "logits")
+    _need(targets, torch.int32, "targets", (rows, T))
+    _need(mask, torch.uint8, "mask", (rows, T))
+    _need(logp_sum, torch.float32, "logp_sum", (rows,))
+    if logp_sum64 is not None:
+        _need(logp_sum64, torch.float64, "logp_sum64", (rows,))
+    if lse is not None:
+        _need(lse, torch.float32, "lse", (rows, T))
+    if n_tokens is not None:
+        _need(n_tokens, torch.int32, "n_tokens", (rows,))
+    _need(workspace, torch.uint8, "workspace")
+    _check(lib().dpo_logits_f32_seq_logps(_ptr(logits), _ptr(targets), _ptr(mask), rows, T, V,
+                                          _ptr(logp_sum), _ptr(logp_sum64), _ptr(lse), _ptr(n_tokens),
+                                          _ptr(workspace), workspace.numel(), _stream(stream, logits)))
+
+
+def dpo_logits_f32_backward(logits, targets, mask, lse, weight, d_logits, workspace=None,
+                            stream=None) -> None:
+    import torch
+    rows, T, V = logits.shape
+    _need(logits, torch.float32, "logits")
+    _need(targets, torch.int32, "targets", (rows, T))
+    _need(mask, torch.uint8, "mask", (rows, T))
+    _need(lse, torch.float32, "lse", (rows, T))
+    _need(weight, torch.float32, "weight", (rows,))
+    _need(d_logits, torch.float32, "d_logits", (rows, T, V))
+    _need(workspace, torch.uint8, "workspace")
+    _check(lib().dpo_logits_f32_backward(_ptr(logits), _ptr(targets), _ptr(mask), rows, T, V, _ptr(lse),
+                                         _ptr(weight), _ptr(d_logits), _ptr(workspace), workspace.numel(),
+                                         _stream(stream, logits)))
+
+
+def dpo_seq_logps_shard(hidden, w_shard, targets, mask, v_begin: int, V_total: int, part_max, part_sumexp,
+                        part_tgt, workspace=None, stream=None) -> None:
+    import torch
+    rows, T, H = hidden.shape
+    Vs = w_shard.shape[0]
+    _need(hidden, torch.bfloat16, "hidden")
+    _need(w_shard, torch.bfloat16, "w_shard", (Vs, H))
+    _need(targets, torch.int32, "targets", (rows, T))
+    _need(mask, torch.uint8, "mask", (rows, T))
+    for t, name in ((part_max, "part_max"), (part_sumexp, "part_sumexp"), (part_tgt, "part_tgt")):
+        _need(t, torch.float32, name, (rows, T))
+    _need(workspace, torch.uint8, "workspace")
+    _check(lib().dpo_seq_logps_shard(_ptr(hidden), _ptr(w_shard), _ptr(targets), _ptr(mask), rows, T, H, Vs,
+                                     int(v_begin), int(V_total), _ptr(part_max), _ptr(part_sumexp),
+                                     _ptr(part_tgt), _ptr(workspace), workspace.numel(),
+                                     _stream(stream, hidden)))
+
+
+def dpo_shard_combine(part_max, part_sumexp, part_tgt, targets, mask, V_total: int, logp_sum, logp_sum64=None,
+                      lse=None, n_tokens=None, workspace=None, stream=None) -> None:
+    import torch
+    S, rows, T = part_max.shape
+    for t, name in ((part_max, "part_max"), (part_sumexp, "part_sumexp"), (part_tgt, "part_tgt")):
+        _need(t, torch.float32, name, (S, rows, T))
+    _need(targets, torch.int32, "targets", (rows, T))
+    _need(mask, torch.uint8, "mask", (rows, T))
+    _need(logp_sum, torch.float32, "logp_sum", (rows,))
+    if logp_sum64 is not None:
+        _need(logp_sum64, torch.float64, "logp_sum64", (rows,))
+    if lse is not None:
+        _need(lse, torch.float32, "lse", (rows, T))
+    if n_tokens is not None:
+        _need(n_tokens, torch.int32, "n_tokens", (rows,))
+    _need(workspace, torch.uint8, "workspace")
+    _check(lib().dpo_shard_combine(_ptr(part_max), _ptr(part_sumexp), _ptr(part_tgt), S, _ptr(targets),
+                                   _ptr(mask), rows, T, int(V_total), _ptr(logp_sum), _ptr(logp_sum64),
+                                   _ptr(lse), _ptr(n_tokens), _ptr(workspace), workspace.numel(),
+                                   _stream(stream, part_max)))
+
+
+def dpo_head_backward_shard(hidden, w_shard, targets, mask, v_begin: int, V_total: int, lse, weight,
+                            d_hidden, d_w_shard, accumulate_dw: int = 0, workspace=None, stream=None) -> None:
+    import torch
+    rows, T, H = hidden.shape
+    Vs = w_shard.shape[0]
+    _need(hidden, torch.bfloat16, "hidden")
+    _need(w_shard, torch.bfloat16, "w_shard", (Vs, H))
+    _need(targets, torch.int32, "targets", (rows, T))
+    _need(mask, torch.uint8, "mask", (rows, T))
+    _need(lse, torch.float32, "lse", (rows, T))
+    _need(weight, torch.float32, "weight", (rows,))
+    _need(d_hidden, torch.float32, "d_hidden", (rows, T, H))
+    _need(d_w_shard, torch.float32, "d_w_shard", (Vs, H))
+    _need(workspace, torch.uint8, "workspace")
+    _check(lib().dpo_head_backward_shard(_ptr(hidden), _ptr(w_shard), _ptr(targets), _ptr(mask), rows, T, H,
+                                         Vs, int(v_begin), int(V_total), _ptr(lse), _ptr(weight),
+                                         _ptr(d_hidden), _ptr(d_w_shard), int(accumulate_dw),
+                                         _ptr(workspace), workspace.numel(), _stream(stream, hidden)))
+
+
+def dpo_seq_logps_metrics(hidden, w_vocab, targets, mask, logp_sum, logit_sum, logp_sum64=None, lse=None,
+                          n_tokens=None, workspace=None, stream=None) -> None:
+    import torch
+    rows, T, H = hidden.shape
+    V = w_vocab.shape[0]
+    _need(hidden, torch.bfloat16, "hidden")
+    _need(w_vocab, torch.bfloat16, "w_vocab", (V, H))
+    _need(targets, torch.int32, "targets", (rows, T))
+    _need(mask, torch.uint8, "mask", (rows, T))
+    _need(logp_sum, torch.float32, "logp_sum", (rows,))
+    _need(logit_sum, torch.float64, "logit_sum", (rows,))
+    if logp_sum64 is not None:
+        _need(logp_sum64, torch.float64, "logp_sum64", (rows,))
+    if lse is not None:
+        _need(lse, torch.float32, "lse", (rows, T))
+    if n_tokens is not None:
+        _need(n_tokens, torch.int32, "n_tokens", (rows,))
+    _need(workspace, torch.uint8, "workspace")
+    _check(lib().dpo_seq_logps_metrics(_ptr(hidden), _ptr(w_vocab), _ptr(targets), _ptr(mask), rows, T, H, V,
+                                       _ptr(logp_sum), _ptr(logp_sum64), _ptr(lse), _ptr(n_tokens),
+                                       _ptr(logit_sum), _ptr(workspace), workspace.numel(),
+                                       _stream(stream, hidden)))
+
+
+def dpo_logits_mean(logit_sum, n_tokens, V: int, layout: int, means, stream=None) -> None:
+    import torch
+    R = logit_sum.shape[0]
+    _need(logit_sum, torch.float64, "logit_sum")
+    _need(n_tokens, torch.int32, "n_tokens", (R,))
+    _need(means, torch.float32, "means", (2,))
+    if R % 2:
+        raise ValueError("rows must be even")
+    _check(lib().dpo_logits_mean(_ptr(logit_sum), _ptr(n_tokens), R // 2, int(V), int(layout), _ptr(means),
+                                 _stream(stream, logit_sum)))
 
 
 def dpo_device_status(workspace, stream=None) -> int:

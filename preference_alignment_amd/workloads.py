@@ -48,6 +48,20 @@ def bf16_rne_bits(x: np.ndarray) -> np.ndarray:
     return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
 
 
+def _normal_f32(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    """The same chunked N(0, std) float32 draws as ``_normal_bf16``, kept in float32."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    pos = 0
+    while pos < n:
+        m = min(_CHUNK, n - pos)
+        x = rng.standard_normal(m, dtype=np.float32)
+        x *= np.float32(std)
+        out[pos:pos + m] = x
+        pos += m
+    return out.reshape(shape)
+
+
 def _normal_bf16(rng: np.random.Generator, shape, std: float,
                  rms_rows: Optional[int] = None) -> np.ndarray:
     """Draw N(0, std) float32 values in fixed-size chunks and round to bf16.
@@ -181,14 +195,22 @@ def make_head_inputs(*, name: str, seed: int, rows: int, T: int, H: int, V: int,
 
 def make_logits_inputs(*, name: str, seed: int, rows: int, T: int, V: int,
                        comp_start: int, logit_std: float = 3.0, beta: float = 0.1,
-                       layout: int = PAIRS_ADJACENT) -> HeadInputs:
-    """Materialised-logits workload: mask = 1 on [comp_start, T) of every row."""
+                       layout: int = PAIRS_ADJACENT, logits_dtype: str = "bf16") -> HeadInputs:
+    """Materialised-logits workload: mask = 1 on [comp_start, T) of every row.
+
+    ``logits_dtype`` "bf16" gives uint16 bf16 bit patterns; "f32" gives the
+    same float32 draws unrounded (a float32 array)."""
     assert rows % 2 == 0 and rows > 0
     rng = np.random.default_rng(seed)
     mask = _mask_from_spans(rows, T, [comp_start] * rows, [T] * rows)
     targets = rng.integers(0, V, size=(rows, T), dtype=np.int32)
     targets = np.where(mask != 0, targets, IGNORE_INDEX).astype(np.int32)
-    logits = _normal_bf16(rng, (rows, T, V), logit_std)
+    if logits_dtype == "f32":
+        logits = _normal_f32(rng, (rows, T, V), logit_std)
+    elif logits_dtype == "bf16":
+        logits = _normal_bf16(rng, (rows, T, V), logit_std)
+    else:
+        raise ValueError("logits_dtype is bf16 or f32")
     ref_noise = rng.standard_normal(rows)
     return HeadInputs(name=name, rows=rows, T=T, H=0, V=V, beta=beta, layout=layout,
                       targets=targets, mask=mask, ref_noise=ref_noise, logits=logits)

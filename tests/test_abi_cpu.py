@@ -90,7 +90,7 @@ def test_backward_and_logits_validation(L):
 
 
 def test_strerror_and_profile_api(L):
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert len(D.dpo_strerror(code)) >= 2
     assert "unknown" in D.dpo_strerror(-99)
     D.dpo_profile_enable(True)
@@ -117,3 +117,68 @@ def test_product_path_has_no_oracle_dependency():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 txt = open(os.path.join(root, fn)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle|import_module\(.oracle", txt, re.M), fn
+
+
+def test_loss_ex_validation(L):
+    f = L.dpo_loss_ex
+    args = [FAKE, FAKE, FAKE, 2, 0.1, 0, 0, 0.0, FAKE, FAKE, None, None, None, None, None]
+
+    def call(**kw):
+        a = list(args)
+        pos = dict(policy=0, ref=1, n=2, pairs=3, beta=4, layout=5, flags=6, alpha=7, nll=13)
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return f(*a)
+
+    assert call(flags=4) == D.DPO_ERR_LAYOUT
+    for alpha in (-1.0, math.nan, math.inf):
+        assert call(alpha=alpha) == D.DPO_ERR_ALPHA
+    assert call(ref=None) == D.DPO_ERR_NULL                      # reference needed without the flag
+    assert call(n=None, flags=D.DPO_LOSS_LENGTH_NORM) == D.DPO_ERR_NULL
+    assert call(n=None, alpha=0.5) == D.DPO_ERR_NULL
+    assert call(n=None, nll=FAKE) == D.DPO_ERR_NULL
+    assert call(beta=0.0) == D.DPO_ERR_BETA
+    assert call(pairs=0) == D.DPO_ERR_SHAPE
+    assert call(layout=3) == D.DPO_ERR_LAYOUT
+
+
+def test_shard_and_f32_and_metrics_validation(L):
+    wsf = D.dpo_workspace_bytes(D.DPO_OP_SEQ_LOGPS, 4, 64, 256, 256)
+    # v_begin + V_shard beyond V_total, negative v_begin
+    base = [FAKE, FAKE, FAKE, FAKE, 4, 64, 256, 256, 0, 1024, FAKE, FAKE, FAKE, FAKE, wsf, None]
+    for vb, vt in [(800, 1024), (-8, 1024), (0, 128)]:
+        a = list(base)
+        a[8], a[9] = vb, vt
+        assert L.dpo_seq_logps_shard(*a) == D.DPO_ERR_SHAPE, (vb, vt)
+    a = list(base)
+    a[12] = None
+    assert L.dpo_seq_logps_shard(*a) == D.DPO_ERR_NULL
+    a = list(base)
+    a[14] = wsf - 1
+    assert L.dpo_seq_logps_shard(*a) == D.DPO_ERR_WORKSPACE
+    wsb = D.dpo_workspace_bytes(D.DPO_OP_HEAD_BACKWARD, 4, 64, 256, 256)
+    bb = [FAKE, FAKE, FAKE, FAKE, 4, 64, 256, 256, 768, 1024, FAKE, FAKE, FAKE, FAKE, 0, FAKE, wsb, None]
+    bb[9] = 1000
+    assert L.dpo_head_backward_shard(*bb) == D.DPO_ERR_SHAPE
+    bb[9] = 1024
+    bb[14] = 3
+    assert L.dpo_head_backward_shard(*bb) == D.DPO_ERR_LAYOUT
+    wsc = D.dpo_workspace_bytes(D.DPO_OP_SHARD_COMBINE, 4, 64, 0, 1024)
+    assert wsc > 0
+    cc = [FAKE, FAKE, FAKE, 0, FAKE, FAKE, 4, 64, 1024, FAKE, None, None, None, FAKE, wsc, None]
+    assert L.dpo_shard_combine(*cc) == D.DPO_ERR_SHAPE
+    cc[3] = 4
+    cc[1] = FAKE + 4
+    assert L.dpo_shard_combine(*cc) == D.DPO_ERR_ALIGN
+    wsl = D.dpo_workspace_bytes(D.DPO_OP_LOGITS_SEQ_LOGPS, 4, 64, 0, 1024)
+    assert L.dpo_logits_f32_seq_logps(FAKE, FAKE, FAKE, 3, 64, 1024, FAKE, None, None, None, FAKE, wsl,
+                                      None) == D.DPO_ERR_SHAPE
+    assert L.dpo_logits_f32_backward(FAKE, FAKE, FAKE, 4, 64, 1024, FAKE, None, FAKE, FAKE, 256,
+                                     None) == D.DPO_ERR_NULL
+    wsm = D.dpo_workspace_bytes(D.DPO_OP_SEQ_LOGPS_METRICS, 4, 64, 256, 1024)
+    assert wsm > D.dpo_workspace_bytes(D.DPO_OP_SEQ_LOGPS, 4, 64, 256, 1024)
+    assert L.dpo_seq_logps_metrics(FAKE, FAKE, FAKE, FAKE, 4, 64, 256, 1024, FAKE, None, None, None, None,
+                                   FAKE, wsm, None) == D.DPO_ERR_NULL
+    assert L.dpo_logits_mean(FAKE, FAKE, 2, 1024, 5, FAKE, None) == D.DPO_ERR_LAYOUT
+    assert L.dpo_logits_mean(FAKE, None, 2, 1024, 0, FAKE, None) == D.DPO_ERR_NULL
+    assert D.dpo_strerror(D.DPO_ERR_ALPHA).startswith("sft_alpha")

@@ -1,0 +1,289 @@
+"""GPU parity of the widened rows against the CPU oracle: the loss variants
+(reference-free, length-normalised, NLL term), the vocabulary-sharded head on
+one GPU's share, the fp32-logits streaming path and the logits-mean
+by-products of the fused forward.  Every call goes through the C ABI."""
+import numpy as np
+import pytest
+
+from oracle import dpo_oracle as O
+from preference_alignment_amd import dpo_head as D
+from preference_alignment_amd import workloads as W
+
+from gpu_common import (GRAD_REL_L2, LOGP_RTOL, LOSS_ATOL, LSE_ATOL, WEIGHT_RTOL, dev_inputs, need_gpu,
+                        np_, rel_l2, run_backward, run_forward, torch)
+
+pytestmark = pytest.mark.gpu
+
+
+def _t(a, dev, dtype=None):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev) if dtype is None else \
+        torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dtype)
+
+
+def _loss_ex(pi64, ref32, n32, beta, layout, flags, alpha, dev):
+    R = pi64.shape[0]
+    o = {k: torch.full(s, float("nan"), dtype=torch.float32, device=dev)
+         for k, s in dict(loss=(1,), weight=(R,), reward=(R,), margin=(R // 2,), accuracy=(1,),
+                          nll=(1,)).items()}
+    D.dpo_loss_ex(pi64, ref32, n32, beta, layout, flags, alpha, o["loss"], o["weight"], o["reward"],
+                  o["margin"], o["accuracy"], o["nll"])
+    return {k: np_(v) for k, v in o.items()}
+
+
+# ----------------------------------------------------------------------------
+# loss variants
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("B", [1, 3, 700])
+def test_loss_variants_match_oracle(B):
+    dev = need_gpu()
+    rng = np.random.default_rng(500 + B)
+    pi = rng.standard_normal(2 * B) * 40 - 600
+    ref = (pi + rng.standard_normal(2 * B) * 3).astype(np.float32)
+    n = rng.integers(1, 900, size=2 * B).astype(np.int32)
+    if B > 1:
+        n[1] = 0  # a row without completion tokens
+    pi_d, ref_d, n_d = _t(pi, dev), _t(ref, dev), _t(n, dev)
+    for layout in (D.DPO_PAIRS_ADJACENT, D.DPO_PAIRS_HALVES):
+        for flags in (0, D.DPO_LOSS_LENGTH_NORM, D.DPO_LOSS_REFERENCE_FREE,
+                      D.DPO_LOSS_LENGTH_NORM | D.DPO_LOSS_REFERENCE_FREE):
+            for alpha in (0.0, 0.7):
+                o = O.dpo_loss_variant(pi, ref.astype(np.float64), n, 0.1, layout,
+                                       length_normalise=bool(flags & D.DPO_LOSS_LENGTH_NORM),
+                                       reference_free=bool(flags & D.DPO_LOSS_REFERENCE_FREE),
+                                       sft_alpha=alpha)
+                g = _loss_ex(pi_d, None if flags & D.DPO_LOSS_REFERENCE_FREE else ref_d, n_d, 0.1, layout,
+                             flags, alpha, dev)
+                key = (layout, flags, alpha)
+                assert abs(float(g["loss"][0]) - o["loss"]) <= LOSS_ATOL * max(1.0, abs(o["loss"])) * 1e-2, key
+                np.testing.assert_allclose(g["weight"], o["weight"], rtol=WEIGHT_RTOL, atol=1e-12, err_msg=str(key))
+                np.testing.assert_allclose(g["reward"], o["reward"], rtol=1e-6, atol=1e-6, err_msg=str(key))
+                np.testing.assert_allclose(g["margin"], o["margin"], rtol=1e-6, atol=1e-6, err_msg=str(key))
+                assert abs(float(g["accuracy"][0]) - o["accuracy"]) < 1e-6, key
+                assert abs(float(g["nll"][0]) - o["nll"]) <= 1e-6 * max(1.0, abs(o["nll"])), key
+
+
+def test_plain_loss_equals_variant_without_flags():
+    dev = need_gpu()
+    rng = np.random.default_rng(7)
+    pi = _t(rng.standard_normal(10) * 20 - 300, dev)
+    ref = _t((rng.standard_normal(10) * 20 - 300).astype(np.float32), dev)
+    R = 10
+    o1 = [torch.empty(s, dtype=torch.float32, device=dev) for s in ((1,), (R,), (R,), (R // 2,), (1,))]
+    o2 = [torch.empty(s, dtype=torch.float32, device=dev) for s in ((1,), (R,), (R,), (R // 2,), (1,))]
+    D.dpo_loss(pi, ref, 0.2, 1, *o1)
+    D.dpo_loss_ex(pi, ref, None, 0.2, 1, 0, 0.0, *o2)
+    for x, y in zip(o1, o2):
+        assert torch.equal(x, y)
+
+
+def test_variant_end_to_end_backward():
+    """Length-normalised loss with an NLL term feeding the unchanged backward."""
+    dev = need_gpu()
+    x = W.make_workload(1)
+    d = dev_inputs(x, dev)
+    fwd = O.seq_logps(x.hidden, x.w_vocab, x.targets, x.mask)
+    ref = (fwd["logp_sum"] + x.ref_noise).astype(np.float32)
+    g = run_forward(x, d, dev)
+    o = O.dpo_loss_variant(fwd["logp_sum"], ref.astype(np.float64), fwd["n_tokens"], x.beta, x.layout,
+                           length_normalise=True, sft_alpha=1.0)
+    gl = _loss_ex(g["logp_sum64"], _t(ref, dev), g["n_tokens"], x.beta, x.layout, D.DPO_LOSS_LENGTH_NORM,
+                  1.0, dev)
+    assert abs(float(gl["loss"][0]) - o["loss"]) <= LOSS_ATOL
+    np.testing.assert_allclose(gl["weight"], o["weight"], rtol=WEIGHT_RTOL, atol=1e-9)
+    dH_o, dW_o = O.head_backward(x.hidden, x.w_vocab, x.targets, x.mask, fwd["lse"], o["weight"])
+    dh, dw = run_backward(x, d, g["lse"], _t(gl["weight"], dev), dev)
+    assert rel_l2(np_(dh), dH_o) <= GRAD_REL_L2
+    assert rel_l2(np_(dw), dW_o) <= GRAD_REL_L2
+
+
+# ----------------------------------------------------------------------------
+# vocabulary shards on one GPU
+# ----------------------------------------------------------------------------
+SHARD_CASES = {
+    # V = 4104 in 4 shards (one of 1032 rows), halves layout, ragged tiles
+    "four_shards": (dict(name="shards4", seed=102, rows=8, T=520, H=320, V=4104, prompt_lo=20, prompt_hi=200,
+                         comp_mode="independent", rms_normalise=True, w_std=0.05, layout=W.PAIRS_HALVES),
+                    [0, 1024, 2056, 3080, 4104]),
+    # a 256-row shard (sort keys reach exactly 256) and a shard smaller than one tile
+    "small_shards": (dict(name="shards_small", seed=110, rows=4, T=96, H=128, V=1024, prompt_lo=8,
+                          prompt_hi=40, w_std=0.2), [0, 256, 512, 1000, 1024]),
+}
+
+
+@pytest.mark.parametrize("case", list(SHARD_CASES))
+def test_vocab_shards_match_oracle(case):
+    dev = need_gpu()
+    kw, cuts = SHARD_CASES[case]
+    x = W.make_head_inputs(**kw)
+    R, T, H, V = x.rows, x.T, x.H, x.V
+    d = dev_inputs(x, dev)
+    hid = O.bf16_to_f64(x.hidden)
+    wf = O.bf16_to_f64(x.w_vocab)
+    m = x.mask != 0
+    S = len(cuts) - 1
+    pmax = torch.empty(S, R, T, dtype=torch.float32, device=dev)
+    psum = torch.empty_like(pmax)
+    ptgt = torch.empty_like(pmax)
+    for s in range(S):
+        a, b = cuts[s], cuts[s + 1]
+        ws = D.alloc_workspace(D.DPO_OP_SEQ_LOGPS, R, T, H, b - a, dev)
+        D.dpo_seq_logps_shard(d["hidden"], d["w"][a:b].contiguous(), d["targets"], d["mask"], a, V,
+                              pmax[s], psum[s], ptgt[s], workspace=ws)
+        D.dpo_device_status(ws)
+        po = O.shard_partials_f64(hid, wf[a:b], x.targets, x.mask, a, V)
+        gm, gs, gt = np_(pmax[s]), np_(psum[s]), np_(ptgt[s])
+        assert np.all(gm[~m] == -np.inf) and np.all(gs[~m] == 0) and np.all(gt[~m] == -np.inf)
+        np.testing.assert_allclose(gm[m], po["max"][m], rtol=0, atol=1e-5)
+        # the shard sums are relative to the shard max: compare log(s) + max
+        np.testing.assert_allclose(np.log(gs[m]) + gm[m], np.log(po["sumexp"][m]) + po["max"][m], rtol=0,
+                                   atol=LSE_ATOL)
+        fin = np.isfinite(po["tgt"])
+        assert np.array_equal(np.isfinite(gt), fin)
+        np.testing.assert_allclose(gt[fin], po["tgt"][fin], rtol=0, atol=1e-5)
+    # combine on the GPU vs the unsharded oracle
+    wsc = D.alloc_workspace(D.DPO_OP_SHARD_COMBINE, R, T, 0, V, dev)
+    ls = torch.empty(R, dtype=torch.float32, device=dev)
+    ls64 = torch.empty(R, dtype=torch.float64, device=dev)
+    lse = torch.empty(R, T, dtype=torch.float32, device=dev)
+    nt = torch.empty(R, dtype=torch.int32, device=dev)
+    D.dpo_shard_combine(pmax, psum, ptgt, d["targets"], d["mask"], V, ls, ls64, lse, nt, workspace=wsc)
+    D.dpo_device_status(wsc)
+    fwd = O.seq_logps(x.hidden, x.w_vocab, x.targets, x.mask)
+    np.testing.assert_array_equal(np_(nt), fwd["n_tokens"])
+    tol = LOGP_RTOL * np.maximum(1.0, np.abs(fwd["logp_sum"]))
+    assert np.all(np.abs(np_(ls64) - fwd["logp_sum"]) <= tol)
+    assert np.max(np.abs(np_(lse)[m] - fwd["lse"][m]), initial=0.0) <= LSE_ATOL
+    assert np.all(np_(lse)[~m] == 0.0)
+    # and against the unsharded GPU path
+    g = run_forward(x, d, dev)
+    assert np.all(np.abs(np_(ls64) - np_(g["logp_sum64"])) <= tol)
+
+    # backward per shard from the combined lse
+    ref = (fwd["logp_sum"] + x.ref_noise).astype(np.float64)
+    ol = O.dpo_loss(fwd["logp_sum"], ref, x.beta, x.layout)
+    weight = _t(ol["weight"].astype(np.float32), dev)
+    dH_o, dW_o = O.head_backward(x.hidden, x.w_vocab, x.targets, x.mask, fwd["lse"], ol["weight"])
+    dh_sum = torch.zeros(R, T, H, dtype=torch.float64, device=dev)
+    dws = []
+    for s in range(S):
+        a, b = cuts[s], cuts[s + 1]
+        ws = D.alloc_workspace(D.DPO_OP_HEAD_BACKWARD, R, T, H, b - a, dev)
+        dh = torch.full((R, T, H), float("nan"), dtype=torch.float32, device=dev)
+        dw = torch.full((b - a, H), float("nan"), dtype=torch.float32, device=dev)
+        D.dpo_head_backward_shard(d["hidden"], d["w"][a:b].contiguous(), d["targets"], d["mask"], a, V, lse,
+                                  weight, dh, dw, 0, workspace=ws)
+        D.dpo_device_status(ws)
+        assert np.all(np_(dh)[~m] == 0.0)
+        # each shard's own terms against the oracle's shard gradient
+        sh_o, sw_o = O.head_backward_shard_f64(hid, wf[a:b], x.targets, x.mask, fwd["lse"], ol["weight"], a, V)
+        assert rel_l2(np_(dw), sw_o) <= GRAD_REL_L2, (s, rel_l2(np_(dw), sw_o))
+        dh_sum += dh.double()
+        dws.append(np_(dw))
+    assert rel_l2(np_(dh_sum), dH_o) <= GRAD_REL_L2, rel_l2(np_(dh_sum), dH_o)
+    assert rel_l2(np.concatenate(dws), dW_o) <= GRAD_REL_L2
+
+
+def test_shard_combine_reports_missing_target_shard():
+    dev = need_gpu()
+    x = W.make_workload(1)
+    R, T, H, V = x.rows, x.T, x.H, x.V
+    d = dev_inputs(x, dev)
+    pm = torch.empty(1, R, T, dtype=torch.float32, device=dev)
+    ps, pt = torch.empty_like(pm), torch.empty_like(pm)
+    ws = D.alloc_workspace(D.DPO_OP_SEQ_LOGPS, R, T, H, 512, dev)
+    D.dpo_seq_logps_shard(d["hidden"], d["w"][:512].contiguous(), d["targets"], d["mask"], 0, V, pm[0], ps[0],
+                          pt[0], workspace=ws)
+    assert D.dpo_device_status(ws) == D.DPO_OK   # foreign targets are no error in a shard
+    wsc = D.alloc_workspace(D.DPO_OP_SHARD_COMBINE, R, T, 0, V, dev)
+    out = torch.empty(R, dtype=torch.float32, device=dev)
+    D.dpo_shard_combine(pm, ps, pt, d["targets"], d["mask"], V, out, workspace=wsc)
+    assert np.any((x.targets >= 512) & (x.mask != 0))
+    with pytest.raises(D.DpoError):
+        D.dpo_device_status(wsc)
+
+
+# ----------------------------------------------------------------------------
+# fp32 logits streaming
+# ----------------------------------------------------------------------------
+F32_CASES = {
+    "small": dict(name="f32_small", seed=120, rows=4, T=64, V=1000, comp_start=10),
+    "odd_vectors": dict(name="f32_odd", seed=121, rows=2, T=33, V=8, comp_start=1),
+    "large_vocab": dict(name="f32_large", seed=122, rows=4, T=48, V=128256, comp_start=16),
+}
+
+
+@pytest.mark.parametrize("case", list(F32_CASES))
+def test_f32_logits_match_oracle(case):
+    dev = need_gpu()
+    x = W.make_logits_inputs(logits_dtype="f32", **F32_CASES[case])
+    R, T, V = x.rows, x.T, x.V
+    lg = _t(x.logits, dev)
+    tg, mk = _t(x.targets, dev), _t(x.mask, dev)
+    ws = D.alloc_workspace(D.DPO_OP_LOGITS_SEQ_LOGPS, R, T, 0, V, dev)
+    ls = torch.empty(R, dtype=torch.float32, device=dev)
+    ls64 = torch.empty(R, dtype=torch.float64, device=dev)
+    lse = torch.empty(R, T, dtype=torch.float32, device=dev)
+    nt = torch.empty(R, dtype=torch.int32, device=dev)
+    D.dpo_logits_f32_seq_logps(lg, tg, mk, ls, ls64, lse, nt, workspace=ws)
+    D.dpo_device_status(ws)
+    fwd = O.logits_f32_seq_logps(x.logits, x.targets, x.mask)
+    m = x.mask != 0
+    np.testing.assert_array_equal(np_(nt), fwd["n_tokens"])
+    tol = LOGP_RTOL * np.maximum(1.0, np.abs(fwd["logp_sum"]))
+    assert np.all(np.abs(np_(ls64) - fwd["logp_sum"]) <= tol)
+    assert np.max(np.abs(np_(lse)[m] - fwd["lse"][m]), initial=0.0) <= LSE_ATOL
+    weight = np.linspace(-0.05, 0.05, R).astype(np.float32)
+    wsb = D.alloc_workspace(D.DPO_OP_LOGITS_BACKWARD, R, T, 0, V, dev)
+    dl = torch.full((R, T, V), float("nan"), dtype=torch.float32, device=dev)
+    D.dpo_logits_f32_backward(lg, tg, mk, lse, _t(weight, dev), dl, workspace=wsb)
+    D.dpo_device_status(wsb)
+    dl = np_(dl).reshape(R * T, V)
+    assert np.all(dl[~m.reshape(-1)] == 0.0)
+    pos = np.arange(R * T) if R * T * V <= 4_000_000 else np.flatnonzero(m.reshape(-1))[::7]
+    want = O.logits_f32_backward_rows(x.logits, x.targets, x.mask, fwd["lse"], weight.astype(np.float64), pos)
+    assert rel_l2(dl[pos], want) <= GRAD_REL_L2, rel_l2(dl[pos], want)
+    # fp32 output: every element within a few fp32 ulps of |w| plus the lse difference
+    err = np.abs(dl[pos] - want)
+    assert np.all(err <= 1e-6 * np.abs(weight).max() + 2e-4 * np.abs(want))
+
+
+# ----------------------------------------------------------------------------
+# logits-mean by-products of the fused forward
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("case", ["workload1", "ragged"])
+def test_logit_sums_and_means(case):
+    dev = need_gpu()
+    if case == "workload1":
+        x = W.make_workload(1)
+    else:
+        x = W.make_head_inputs(name="ragged_small", seed=101, rows=6, T=300, H=192, V=1000, prompt_lo=10,
+                               prompt_hi=120, comp_mode="independent", targets_dist="zipf")
+    R, T, H, V = x.rows, x.T, x.H, x.V
+    d = dev_inputs(x, dev)
+    ws = D.alloc_workspace(D.DPO_OP_SEQ_LOGPS_METRICS, R, T, H, V, dev)
+    ls = torch.empty(R, dtype=torch.float32, device=dev)
+    ls64 = torch.empty(R, dtype=torch.float64, device=dev)
+    lse = torch.empty(R, T, dtype=torch.float32, device=dev)
+    nt = torch.empty(R, dtype=torch.int32, device=dev)
+    zs = torch.full((R,), float("nan"), dtype=torch.float64, device=dev)
+    D.dpo_seq_logps_metrics(d["hidden"], d["w"], d["targets"], d["mask"], ls, zs, ls64, lse, nt, workspace=ws)
+    D.dpo_device_status(ws)
+    hid = O.bf16_to_f64(x.hidden)
+    wf = O.bf16_to_f64(x.w_vocab)
+    want = O.logit_row_sums_f64(hid, wf, x.mask)
+    # scale: the sum of |z| over the row's completion logits
+    Z = np.einsum("rth,vh->rtv", hid, wf) if R * T * V <= 3_000_000 else None
+    if Z is not None:
+        scale = np.array([np.abs(Z[r][x.mask[r] != 0]).sum() for r in range(R)])
+    else:
+        scale = np.abs(want) + 1.0
+    assert np.all(np.abs(np_(zs) - want) <= 1e-5 * np.maximum(scale, 1.0)), (np_(zs), want)
+    # the other outputs are those of the plain forward, bit for bit
+    g = run_forward(x, d, dev)
+    assert torch.equal(ls64, g["logp_sum64"]) and torch.equal(lse, g["lse"]) and torch.equal(nt, g["n_tokens"])
+    means = torch.empty(2, dtype=torch.float32, device=dev)
+    D.dpo_logits_mean(zs, nt, V, x.layout, means)
+    wc, wr = O.logits_means(want, x.mask.sum(axis=1), V, x.layout)
+    mscale = 1e-5 * max(1.0, scale.max() / max(1, x.mask.sum()) / V)
+    assert abs(float(np_(means)[0]) - wc) <= mscale + 1e-6 * abs(wc)
+    assert abs(float(np_(means)[1]) - wr) <= mscale + 1e-6 * abs(wr)
