@@ -43,7 +43,8 @@ CSRC = os.path.join(ROOT, "preference_alignment_amd", "csrc")
 FAMILIES = {"head": ["dpo_common.h", "gemm_core.h", "kernels_head.hip", "launch.h"],
             "stream": ["dpo_common.h", "kernels_stream.hip", "launch.h"]}
 KERNEL_FAMILY = {"fwd_gemm": "head", "dlogits_gemm": "head", "dhidden_gemm": "head", "dw_gemm": "head",
-                 "stream_fwd": "stream", "stream_bwd": "stream"}
+                 "stream_fwd": "stream", "stream_bwd": "stream", "stream_fwd_f32": "stream",
+                 "stream_bwd_f32": "stream"}
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 
 
@@ -59,6 +60,12 @@ def source_digest(family):
 
 
 def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` (a label such as "2" or
+    "5 f32") from the committed counter table; see _measured_traffic."""
+    return _measured_traffic(kernel, str(workload))
+
+
+def _measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE counters,
     scaled by the copy calibration; None when absent or when the kernel's
     sources changed since the counters were taken."""
@@ -75,12 +82,23 @@ def measured_traffic(kernel, workload):
                     scale[key] = float(line.split(":", 1)[1])
             if line.startswith("|") and not line.startswith("|---"):
                 c = [x.strip() for x in line.strip("|").split("|")]
-                if len(c) >= 6 and c[0] in KERNEL_FAMILY and c[1].isdigit():
-                    rows[(c[0], int(c[1]))] = (c[2], c[3], float(c[4]), float(c[5]))
+                if len(c) >= 6 and c[0] in KERNEL_FAMILY:
+                    rows[(c[0], c[1])] = (c[2], c[3], float(c[4]), float(c[5]))
     r = rows.get((kernel, workload))
     if r is None or len(scale) != 2 or r[0] != fam or r[1] != source_digest(fam):
         return None
     return (r[2] * scale["fetch_scale"] + r[3] * scale["write_scale"]) * 1024.0
+
+
+ROWS = ["main", "loss-variant", "vocab-shard", "f32-logits", "logits-means"]
+ROW_METRICS = {
+    "loss-variant": "completion tokens/s, fused head fwd+bwd with the length-normalised loss and NLL term "
+                    "@H{H} V{V}; % MFMA peak",
+    "vocab-shard": "completion tokens/s, one GPU's V/4 vocabulary shard (TP=4 share) fwd+combine+bwd "
+                   "@H{H} V{Vs} of {V}; % MFMA peak",
+    "f32-logits": "completion tokens/s, materialised fp32 logits fwd+bwd @V{V}; % HBM peak",
+    "logits-means": "completion tokens/s, fused head fwd+bwd with logits-mean sums @H{H} V{V}; % MFMA peak",
+}
 
 
 def parse():
@@ -93,6 +111,12 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=256)
     p.add_argument("--no-kernel-timing", action="store_true")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
+    p.add_argument("--row", default="main", choices=ROWS,
+                   help="main: the fused step (or the streaming step for workload 5); loss-variant: "
+                        "length-normalised loss with an NLL term (alpha 1); vocab-shard: one GPU's quarter "
+                        "of the vocabulary (TP=4 share) with the shard combine; f32-logits: the streaming "
+                        "step on fp32 logits of workload 5's shape; logits-means: the fused step with the "
+                        "logits-mean sums")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of this many MiB (5 times), to scale "
                         "hardware byte counters")
@@ -107,15 +131,18 @@ def bf(a, dev):
 class HeadStep:
     """Buffers and the call sequence of one fused step (all work in the HIP library)."""
 
-    def __init__(self, x, dev, forward_only=False):
+    def __init__(self, x, dev, forward_only=False, loss_variant=False, metrics=False):
         import torch
         from preference_alignment_amd import dpo_head as D
         self.D, self.x, self.fwd_only = D, x, forward_only
+        self.loss_variant, self.metrics = loss_variant, metrics
         R, T, H, V = x.rows, x.T, x.H, x.V
         self.hidden, self.w = bf(x.hidden, dev), bf(x.w_vocab, dev)
         self.targets = torch.from_numpy(x.targets).to(dev)
         self.mask = torch.from_numpy(x.mask).to(dev)
         op = D.DPO_OP_REF_SCORE if forward_only else D.DPO_OP_SEQ_LOGPS
+        if metrics:
+            op = D.DPO_OP_SEQ_LOGPS_METRICS
         self.ws_f = D.alloc_workspace(op, R, T, H, V, dev)
         self.s32 = torch.empty(R, dtype=torch.float32, device=dev)
         if forward_only:
@@ -127,9 +154,12 @@ class HeadStep:
         self.weight = torch.empty(R, dtype=torch.float32, device=dev)
         self.dh = torch.empty(R, T, H, dtype=torch.float32, device=dev)
         self.dw = torch.empty(V, H, dtype=torch.float32, device=dev)
+        self.ntok = torch.empty(R, dtype=torch.int32, device=dev)
+        self.zsum = torch.empty(R, dtype=torch.float64, device=dev)
+        self.means = torch.empty(2, dtype=torch.float32, device=dev)
         # reference sums: the policy sums of this batch plus N(0,1) noise
         D.dpo_seq_logps(self.hidden, self.w, self.targets, self.mask, self.s32, self.s64, self.lse,
-                        workspace=self.ws_f)
+                        self.ntok, workspace=self.ws_f)
         D.dpo_device_status(self.ws_f)
         self.ref = (self.s64 + torch.from_numpy(x.ref_noise).to(dev)).float()
 
@@ -138,9 +168,18 @@ class HeadStep:
         if self.fwd_only:
             D.dpo_ref_score(self.hidden, self.w, self.targets, self.mask, self.s32, workspace=self.ws_f)
             return
-        D.dpo_seq_logps(self.hidden, self.w, self.targets, self.mask, self.s32, self.s64, self.lse,
-                        workspace=self.ws_f)
-        D.dpo_loss(self.s64, self.ref, x.beta, x.layout, self.loss, self.weight)
+        if self.metrics:
+            D.dpo_seq_logps_metrics(self.hidden, self.w, self.targets, self.mask, self.s32, self.zsum,
+                                    self.s64, self.lse, self.ntok, workspace=self.ws_f)
+            D.dpo_logits_mean(self.zsum, self.ntok, x.V, x.layout, self.means)
+        else:
+            D.dpo_seq_logps(self.hidden, self.w, self.targets, self.mask, self.s32, self.s64, self.lse,
+                            self.ntok, workspace=self.ws_f)
+        if self.loss_variant:
+            D.dpo_loss_ex(self.s64, self.ref, self.ntok, x.beta, x.layout, D.DPO_LOSS_LENGTH_NORM, 1.0,
+                          self.loss, self.weight)
+        else:
+            D.dpo_loss(self.s64, self.ref, x.beta, x.layout, self.loss, self.weight)
         D.dpo_head_backward(self.hidden, self.w, self.targets, self.mask, self.lse, self.weight, self.dh,
                             self.dw, 0, workspace=self.ws_b)
 
@@ -151,7 +190,10 @@ class LogitsStep:
         from preference_alignment_amd import dpo_head as D
         self.D, self.x = D, x
         R, T, V = x.rows, x.T, x.V
-        self.logits = bf(x.logits, dev)
+        self.f32 = x.logits.dtype == np.float32
+        self.logits = torch.from_numpy(x.logits).to(dev) if self.f32 else bf(x.logits, dev)
+        fwd = D.dpo_logits_f32_seq_logps if self.f32 else D.dpo_logits_seq_logps
+        self.fwd, self.bwd = fwd, (D.dpo_logits_f32_backward if self.f32 else D.dpo_logits_backward)
         self.targets = torch.from_numpy(x.targets).to(dev)
         self.mask = torch.from_numpy(x.mask).to(dev)
         self.ws_f = D.alloc_workspace(D.DPO_OP_LOGITS_SEQ_LOGPS, R, T, 0, V, dev)
@@ -161,22 +203,71 @@ class LogitsStep:
         self.lse = torch.empty(R, T, dtype=torch.float32, device=dev)
         self.loss = torch.empty(1, dtype=torch.float32, device=dev)
         self.weight = torch.empty(R, dtype=torch.float32, device=dev)
-        self.dl = torch.empty(R, T, V, dtype=torch.bfloat16, device=dev)
-        D.dpo_logits_seq_logps(self.logits, self.targets, self.mask, self.s32, self.s64, self.lse,
-                               workspace=self.ws_f)
+        self.dl = torch.empty(R, T, V, dtype=torch.float32 if self.f32 else torch.bfloat16, device=dev)
+        self.fwd(self.logits, self.targets, self.mask, self.s32, self.s64, self.lse, workspace=self.ws_f)
         D.dpo_device_status(self.ws_f)
         self.ref = (self.s64 + torch.from_numpy(x.ref_noise).to(dev)).float()
 
     def step(self):
         D, x = self.D, self.x
-        D.dpo_logits_seq_logps(self.logits, self.targets, self.mask, self.s32, self.s64, self.lse,
-                               workspace=self.ws_f)
+        self.fwd(self.logits, self.targets, self.mask, self.s32, self.s64, self.lse, workspace=self.ws_f)
         D.dpo_loss(self.s64, self.ref, x.beta, x.layout, self.loss, self.weight)
-        D.dpo_logits_backward(self.logits, self.targets, self.mask, self.lse, self.weight, self.dl,
-                              workspace=self.ws_b)
+        self.bwd(self.logits, self.targets, self.mask, self.lse, self.weight, self.dl, workspace=self.ws_b)
 
 
-def cpu_baseline(x, k, sample_tokens):
+class ShardStep:
+    """One GPU's share of a head whose vocabulary is split in `shards` equal
+    slices: this GPU's slice forward, the combine of all slices' partials
+    (the other slices' partials stand for what an all-gather would bring and
+    are computed once at set-up), the loss, and this slice's backward."""
+
+    def __init__(self, x, dev, shards=4):
+        import torch
+        from preference_alignment_amd import dpo_head as D
+        self.D, self.x = D, x
+        R, T, H, V = x.rows, x.T, x.H, x.V
+        assert V % (8 * shards) == 0
+        self.Vs = V // shards
+        w = bf(x.w_vocab, dev)
+        self.w_shard = w[:self.Vs].contiguous()
+        self.hidden = bf(x.hidden, dev)
+        self.targets = torch.from_numpy(x.targets).to(dev)
+        self.mask = torch.from_numpy(x.mask).to(dev)
+        self.ws_f = D.alloc_workspace(D.DPO_OP_SEQ_LOGPS, R, T, H, self.Vs, dev)
+        self.ws_c = D.alloc_workspace(D.DPO_OP_SHARD_COMBINE, R, T, 0, V, dev)
+        self.ws_b = D.alloc_workspace(D.DPO_OP_HEAD_BACKWARD, R, T, H, self.Vs, dev)
+        self.pm = torch.empty(shards, R, T, dtype=torch.float32, device=dev)
+        self.ps = torch.empty_like(self.pm)
+        self.pt = torch.empty_like(self.pm)
+        for s in range(shards):
+            ws = self.ws_f
+            D.dpo_seq_logps_shard(self.hidden, w[s * self.Vs:(s + 1) * self.Vs].contiguous(), self.targets,
+                                  self.mask, s * self.Vs, V, self.pm[s], self.ps[s], self.pt[s], workspace=ws)
+        del w
+        self.s32 = torch.empty(R, dtype=torch.float32, device=dev)
+        self.s64 = torch.empty(R, dtype=torch.float64, device=dev)
+        self.lse = torch.empty(R, T, dtype=torch.float32, device=dev)
+        self.loss = torch.empty(1, dtype=torch.float32, device=dev)
+        self.weight = torch.empty(R, dtype=torch.float32, device=dev)
+        self.dh = torch.empty(R, T, H, dtype=torch.float32, device=dev)
+        self.dw = torch.empty(self.Vs, H, dtype=torch.float32, device=dev)
+        D.dpo_shard_combine(self.pm, self.ps, self.pt, self.targets, self.mask, V, self.s32, self.s64, self.lse,
+                            workspace=self.ws_c)
+        D.dpo_device_status(self.ws_c)
+        self.ref = (self.s64 + torch.from_numpy(x.ref_noise).to(dev)).float()
+
+    def step(self):
+        D, x = self.D, self.x
+        D.dpo_seq_logps_shard(self.hidden, self.w_shard, self.targets, self.mask, 0, x.V, self.pm[0], self.ps[0],
+                              self.pt[0], workspace=self.ws_f)
+        D.dpo_shard_combine(self.pm, self.ps, self.pt, self.targets, self.mask, x.V, self.s32, self.s64, self.lse,
+                            workspace=self.ws_c)
+        D.dpo_loss(self.s64, self.ref, x.beta, x.layout, self.loss, self.weight)
+        D.dpo_head_backward_shard(self.hidden, self.w_shard, self.targets, self.mask, 0, x.V, self.lse,
+                                  self.weight, self.dh, self.dw, 0, workspace=self.ws_b)
+
+
+def cpu_baseline(x, k, sample_tokens, row="main", shard_rows=None):
     """The oracle, as it stands, on a bounded sample: the first pair of the
     workload with each row cut to its first `sample_tokens` completion positions."""
     from oracle import dpo_oracle as O
@@ -193,20 +284,45 @@ def cpu_baseline(x, k, sample_tokens):
     tg = np.where(mask != 0, x.targets[rows], -100)
     n = int(mask.astype(np.int64).sum())
     t0 = time.perf_counter()
-    if x.logits is not None:
+    if x.logits is not None and x.logits.dtype == np.float32:
+        fwd = O.logits_f32_seq_logps(x.logits[rows], tg, mask)
+        loss = O.dpo_loss(fwd["logp_sum"], fwd["logp_sum"] + x.ref_noise[rows], x.beta, x.layout)
+        O.logits_f32_backward_rows(x.logits[rows], tg, mask, fwd["lse"], loss["weight"], np.arange(2 * x.T))
+        what = "fp32 logits fwd+loss+bwd"
+    elif x.logits is not None:
         fwd = O.logits_seq_logps(x.logits[rows], tg, mask)
         loss = O.dpo_loss(fwd["logp_sum"], fwd["logp_sum"] + x.ref_noise[rows], x.beta, x.layout)
         O.logits_backward_rows(x.logits[rows], tg, mask, fwd["lse"], loss["weight"],
                                np.arange(2 * x.T))
         what = "fwd+loss+bwd"
+    elif row == "vocab-shard":
+        hid = O.bf16_to_f64(x.hidden[rows])
+        ws = O.bf16_to_f64(x.w_vocab[:shard_rows])
+        O.shard_partials_f64(hid, ws, tg, mask, 0, x.V)
+        t_fwd = time.perf_counter() - t0
+        # the other shards' share of the combined lse, untimed
+        fwd = O.seq_logps(x.hidden[rows], x.w_vocab, tg, mask)
+        t1 = time.perf_counter()
+        loss = O.dpo_loss(fwd["logp_sum"], fwd["logp_sum"] + x.ref_noise[rows], x.beta, x.layout)
+        O.head_backward_shard_f64(hid, ws, tg, mask, fwd["lse"], loss["weight"], 0, x.V)
+        t0 = t1 - t_fwd
+        what = "one V/4 shard: fwd partials + loss + bwd (the whole-vocabulary lse it needs is computed untimed)"
     elif k == 3:
         O.seq_logps(x.hidden[rows], x.w_vocab, tg, mask)
         what = "fwd"
     else:
         fwd = O.seq_logps(x.hidden[rows], x.w_vocab, tg, mask)
-        loss = O.dpo_loss(fwd["logp_sum"], fwd["logp_sum"] + x.ref_noise[rows], x.beta, x.layout)
+        if row == "logits-means":
+            sums = O.logit_row_sums_f64(O.bf16_to_f64(x.hidden[rows]), O.bf16_to_f64(x.w_vocab), mask)
+            O.logits_means(sums, fwd["n_tokens"], x.V, x.layout)
+        if row == "loss-variant":
+            loss = O.dpo_loss_variant(fwd["logp_sum"], fwd["logp_sum"] + x.ref_noise[rows], fwd["n_tokens"], x.beta,
+                                      x.layout, length_normalise=True, sft_alpha=1.0)
+        else:
+            loss = O.dpo_loss(fwd["logp_sum"], fwd["logp_sum"] + x.ref_noise[rows], x.beta, x.layout)
         O.head_backward(x.hidden[rows], x.w_vocab, tg, mask, fwd["lse"], loss["weight"])
-        what = "fwd+loss+bwd"
+        what = "fwd+loss+bwd" + ({"logits-means": " with logits-mean sums",
+                                   "loss-variant": " with the length-normalised loss and NLL term"}.get(row, ""))
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "completion tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first pair, {sample_tokens} completion positions per row ({n} tokens), "
@@ -233,14 +349,29 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
         return
     D.lib()  # fail loudly if the HIP library is missing
-    x = W.make_workload(a.workload)
+    row = a.row
+    if row == "f32-logits":
+        a.workload = 5
+    if row in ("loss-variant", "vocab-shard", "logits-means") and a.workload not in (2, 4):
+        print(json.dumps({"error": f"--row {row} runs on the fused head workloads 2 or 4"}))
+        sys.exit(2)
+    if row == "f32-logits":
+        _, kw = W.WORKLOADS[5]
+        kw = {k: v for k, v in kw.items() if k != "kind"}
+        x = W.make_logits_inputs(name="workload5", seed=5, logits_dtype="f32", **kw)
+    else:
+        x = W.make_workload(a.workload)
     n_c = x.n_completion
-    print(f"[bench] workload {a.workload}: {W.WORKLOADS[a.workload][0]}; N_c={n_c}", file=sys.stderr,
+    print(f"[bench] workload {a.workload}: {W.WORKLOADS[a.workload][0]}; N_c={n_c}; row {row}", file=sys.stderr,
           flush=True)
+    shards = 4
     if a.workload == 5:
         runner = LogitsStep(x, dev)
+    elif row == "vocab-shard":
+        runner = ShardStep(x, dev, shards)
     else:
-        runner = HeadStep(x, dev, forward_only=(a.workload == 3))
+        runner = HeadStep(x, dev, forward_only=(a.workload == 3), loss_variant=(row == "loss-variant"),
+                          metrics=(row == "logits-means"))
 
     for _ in range(a.warmup):
         runner.step()
@@ -266,28 +397,33 @@ def main():
     value = n_c * a.steps / (ms / 1e3)
 
     H, V = x.H, x.V
+    label = str(a.workload) + {"main": "", "f32-logits": " f32", "vocab-shard": " shard4",
+                               "loss-variant": " loss-variant", "logits-means": " logits-means"}[row]
     kern_avg = {k: (v[0] / v[1], v[1]) for k, v in kernels.items()}
     if a.workload == 5:
         E = x.rows * x.T * V
-        per_kernel_bytes = {"stream_fwd": n_c * V * 2.0, "stream_bwd": n_c * V * 2.0 + E * 2.0}
-        dom = max(per_kernel_bytes, key=lambda k: kern_avg.get(k, (0,))[0]) if kern_avg else "stream_bwd"
+        eb = 4.0 if row == "f32-logits" else 2.0
+        sfx = "_f32" if row == "f32-logits" else ""
+        per_kernel_bytes = {"stream_fwd" + sfx: n_c * V * eb, "stream_bwd" + sfx: n_c * V * eb + E * eb}
+        dom = max(per_kernel_bytes, key=lambda k: kern_avg.get(k, (0,))[0]) if kern_avg else "stream_bwd" + sfx
         avg = kern_avg[dom][0] if dom in kern_avg else None
         ach = per_kernel_bytes[dom] / (avg / 1e3) / 1e9 if avg else None
         roof = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": ach / PEAK_HBM_GBS if ach else None,
-                "traffic": measured_traffic(dom, a.workload), "avg_ms": avg,
+                "traffic": measured_traffic(dom, label), "avg_ms": avg,
                 "algorithmic_bytes_per_launch": per_kernel_bytes[dom]}
-        step_bytes = n_c * V * 2.0 * 2 + E * 2.0
+        step_bytes = n_c * V * eb * 2 + E * eb
         extra = {"step_hbm_frac": step_bytes / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS}
     else:
         gemms = ["fwd_gemm"] if a.workload == 3 else ["fwd_gemm", "dlogits_gemm", "dhidden_gemm", "dw_gemm"]
-        flops = 2.0 * n_c * H * V
+        Vw = runner.Vs if row == "vocab-shard" else V
+        flops = 2.0 * n_c * H * Vw
         dom = max(gemms, key=lambda k: kern_avg.get(k, (0,))[0]) if kern_avg else gemms[0]
         avg = kern_avg[dom][0] if dom in kern_avg else None
         ach = flops / (avg / 1e3) / 1e12 if avg else None
         roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS if ach else None,
-                "traffic": measured_traffic(dom, a.workload), "avg_ms": avg,
+                "traffic": measured_traffic(dom, label), "avg_ms": avg,
                 "algorithmic_flops_per_launch": flops}
         step_flops = flops * len(gemms)
         extra = {"step_mfma_frac": step_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -297,15 +433,21 @@ def main():
     cpu = None
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(x, a.workload, a.cpu_sample_tokens)
+        cpu = cpu_baseline(x, a.workload, a.cpu_sample_tokens, row,
+                           runner.Vs if row == "vocab-shard" else None)
 
+    metric = METRICS[a.workload] if row == "main" else ROW_METRICS[row].format(
+        H=H, V=V, Vs=getattr(runner, "Vs", V))
     line = {
-        "metric": METRICS[a.workload], "value": value, "unit": "completion tokens/s", "n_gpus": 1,
+        "metric": metric, "value": value, "unit": "completion tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"workload{a.workload}: {W.WORKLOADS[a.workload][0]}", "rows": x.rows,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if row == "f32-logits" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"workload{a.workload}: {W.WORKLOADS[a.workload][0]}"
+                               + ("" if row == "main" else f"; row {row}"), "rows": x.rows,
                    "seq_len": x.T, "hidden": H, "vocab": V, "completion_tokens": n_c,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU" if row != "vocab-shard" else
+                   f"one GPU's share of a {shards}-way vocabulary split (V/{shards} = {runner.Vs})"},
         "roofline": roof, "cpu_baseline": cpu,
         "kernels_ms_avg": {k: round(v[0], 4) for k, v in kern_avg.items()},
         "host_wall_s": t_host,

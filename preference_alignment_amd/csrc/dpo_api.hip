@@ -302,6 +302,8 @@ int enqueue_fused_forward(const dpo_bf16* hidden, const dpo_bf16* w, const int32
   c.lse64 = at<double>(ws, L.lse64);
   c.logp64 = at<double>(ws, L.logp64);
   c.lse_out = lse;
+  c.part_z = f.part_z;
+  c.zsum64 = f.part_z ? at<double>(ws, L.zsum64) : nullptr;
   RUN("combine", launch_combine(c, st));
   RowSumArgs r;
   r.logp64 = c.logp64;
@@ -313,15 +315,8 @@ int enqueue_fused_forward(const dpo_bf16* hidden, const dpo_bf16* w, const int32
   r.n_tokens = n_tokens;
   RUN("row_sums", launch_row_sums(r, st));
   if (logit_sum) {
-    ZsumArgs z;
-    z.part_z = f.part_z;
-    z.hdr = f.hdr;
-    z.Mp = L.Mp;
-    z.nVt = L.nVt;
-    z.zsum64 = at<double>(ws, L.zsum64);
-    RUN("logit_sums", launch_zsum(z, st));
     RowSumArgs q;
-    q.logp64 = z.zsum64;
+    q.logp64 = c.zsum64;
     q.row_off = r.row_off;
     q.hdr = f.hdr;
     q.rows = rows;

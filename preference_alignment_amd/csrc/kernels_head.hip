@@ -16,6 +16,7 @@
 //   k_fwd_gemm       Z tile = Hc . W^T on MFMA; epilogue: per-row (max, sum exp) over
 //                    the tile's columns and capture of the target logit
 //   k_combine        combine of the per-tile (max, sum exp), fp64 sums -> lse, log p
+//                    (and of the per-tile logit sums, when asked for)
 //   k_row_sums       fp64 per-row sums in a fixed order
 //   k_transpose_w    W^T (bf16) for the dHidden contraction
 //   k_gather_ht      Hc^T (bf16) for the dW contraction
@@ -215,6 +216,7 @@ constexpr int kCombGroups = 16;
 __global__ __launch_bounds__(kCombPos * kCombGroups) void k_combine(CombineArgs a) {
   __shared__ float red_m[kCombGroups][kCombPos];
   __shared__ double red_s[kCombGroups][kCombPos];
+  __shared__ double red_z[kCombGroups][kCombPos];
   const int p = threadIdx.x % kCombPos, g = threadIdx.x / kCombPos;
   const int m = blockIdx.x * kCombPos + p;
   const int n_c = a.hdr->n_c;
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(kCombPos * kCombGroups) void k_combine(CombineArgs 
   __syncthreads();
   M = red_m[0][p];
   for (int q = 1; q < kCombGroups; ++q) M = fmaxf(M, red_m[q][p]);
-  double S = 0.0;
+  double S = 0.0, Z = 0.0;
   if (live) {
     const float Ml = M * kLog2e;
 #pragma unroll 4
@@ -237,8 +239,11 @@ __global__ __launch_bounds__(kCombPos * kCombGroups) void k_combine(CombineArgs 
       const float2 t = a.part[(size_t)j * a.Mp + m];
       S += (double)(t.y * fast_exp2(fmaf(t.x, kLog2e, -Ml)));
     }
+    if (a.part_z)
+      for (int j = g; j < a.nVt; j += kCombGroups) Z += (double)a.part_z[(size_t)j * a.Mp + m];
   }
   red_s[g][p] = S;
+  if (a.part_z) red_z[g][p] = Z;
   __syncthreads();
   if (g == 0 && live) {
     S = red_s[0][p];
@@ -248,6 +253,11 @@ __global__ __launch_bounds__(kCombPos * kCombGroups) void k_combine(CombineArgs 
     a.lse64[m] = lse;
     a.logp64[m] = t >= 0 ? (double)a.tgt_logit[m] - lse : __builtin_nan("");
     if (a.lse_out) a.lse_out[a.idx[m]] = (float)lse;
+    if (a.part_z) {
+      Z = red_z[0][p];
+      for (int q = 1; q < kCombGroups; ++q) Z += red_z[q][p];
+      a.zsum64[m] = Z;
+    }
   }
 }
 
@@ -273,15 +283,6 @@ __global__ __launch_bounds__(256) void k_row_sums(RowSumArgs a) {
     if (a.sum64) a.sum64[r] = v;
     if (a.n_tokens) a.n_tokens[r] = hi - lo;
   }
-}
-
-// per position: the sum of its V logits from the per-tile sums, fp64, tiles in order
-__global__ __launch_bounds__(256) void k_zsum(ZsumArgs a) {
-  const int m = blockIdx.x * 256 + threadIdx.x;
-  if (m >= a.hdr->n_c) return;
-  double z = 0.0;
-  for (int j = 0; j < a.nVt; ++j) z += (double)a.part_z[(size_t)j * a.Mp + m];
-  a.zsum64[m] = z;
 }
 
 // ---------------------------------------------------------------------------
@@ -825,11 +826,6 @@ hipError_t launch_fwd_gemm(const FwdArgs& a, int grid, hipStream_t s) {
     hipLaunchKernelGGL(k_fwd_gemm<true>, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
   else
     hipLaunchKernelGGL(k_fwd_gemm<false>, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_zsum(const ZsumArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_zsum, dim3(a.Mp / 256), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -42,13 +42,6 @@ struct FwdArgs {
   float* part_z;     // [nVt, Mp] per-tile sum of the logits, or NULL
 };
 
-struct ZsumArgs {
-  const float* part_z;  // [nVt, Mp]
-  const WsHeader* hdr;
-  int Mp, nVt;
-  double* zsum64;  // [Mp] per position: sum of its V logits
-};
-
 // one vocabulary shard's (max, sum exp, target logit) per position, [rows*T]
 struct ShardPartialArgs {
   const float2* part;
@@ -86,6 +79,8 @@ struct CombineArgs {
   double* lse64;   // [Mp]
   double* logp64;  // [Mp]
   float* lse_out;  // [rows*T] nullable
+  const float* part_z;  // [nVt, Mp] per-tile logit sums, or NULL
+  double* zsum64;       // [Mp] per position: sum of its V logits (with part_z)
 };
 
 struct RowSumArgs {
@@ -247,7 +242,6 @@ hipError_t launch_stream_fwd(const StreamFwdArgs& a, long positions, hipStream_t
 hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, hipStream_t s);
 hipError_t launch_reset_status(WsHeader* hdr, hipStream_t s);
 hipError_t launch_loss(const LossArgs& a, hipStream_t s);
-hipError_t launch_zsum(const ZsumArgs& a, hipStream_t s);
 hipError_t launch_shard_partials(const ShardPartialArgs& a, int Mp, hipStream_t s);
 hipError_t launch_shard_combine(const ShardCombineArgs& a, int Mp, hipStream_t s);
 hipError_t launch_stream_fwd_f32(const StreamFwdArgs& a, long positions, hipStream_t s);
