@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -24,6 +25,10 @@ constexpr int kGroupBwd = 4;
 // The dHidden contraction has few output tiles (positions x H); splitting its
 // K = vocabulary range in two keeps every CU busy through the last round.
 constexpr int kSplitDh = 2;
+// The backward holds the bf16 softmax part of dlogits (D and D^T) only for one
+// slice of the vocabulary at a time: each of D and D^T stays under this many
+// bytes (balanced slices of whole 256-wide tiles).
+constexpr size_t kChunkBytes = size_t(1) << 30;
 
 // ---------------------------------------------------------------------------
 // workspace layout
@@ -32,6 +37,8 @@ struct Layout {
   int Mp = 0;   // completion positions rounded up to the GEMM tile (upper bound rows*T)
   int Vp = 0;   // vocabulary rounded up to the GEMM tile
   int nVt = 0;  // vocabulary tiles of the forward contraction
+  int chunk_tiles = 0;  // vocabulary tiles per backward slice
+  int n_chunks = 0;
   size_t hdr = 0, idx = 0, tgt = 0, rowc = 0, rowoff = 0;
   size_t part = 0, tlogit = 0, lse64 = 0, logp64 = 0, partz = 0, zsum64 = 0;
   size_t D = 0, DT = 0, WT = 0, HT = 0;
@@ -92,8 +99,13 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     L.logp64 = take((size_t)L.Mp * 8);
   }
   if (op == DPO_OP_HEAD_BACKWARD) {
-    L.D = take((size_t)L.Mp * L.Vp * 2);
-    L.DT = take((size_t)L.Vp * L.Mp * 2);
+    const size_t tile_bytes = (size_t)L.Mp * gemm::BN * 2;
+    const int max_tiles = (int)std::max<size_t>(1, std::min<size_t>(L.nVt, kChunkBytes / tile_bytes));
+    L.n_chunks = cdiv(L.nVt, max_tiles);
+    L.chunk_tiles = cdiv(L.nVt, L.n_chunks);
+    const size_t Vcp = (size_t)L.chunk_tiles * gemm::BN;
+    L.D = take((size_t)L.Mp * Vcp * 2);
+    L.DT = take(Vcp * L.Mp * 2);
     L.WT = take((size_t)H * L.Vp * 2);
     L.HT = take((size_t)H * L.Mp * 2);
     L.keysA = take((size_t)L.Mp * 4);
@@ -583,43 +595,70 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
   GatherHTArgs gh{hidden, at<int>(ws, L.idx), hdr, H, L.Mp, HT};
   RUN("gather_ht", launch_gather_ht(gh, st));
 
-  DProdArgs dp;
-  dp.hidden = hidden;
-  dp.w = w_vocab;
-  dp.hidden_bytes = (unsigned)((size_t)rows * T * H * 2);
-  dp.H = H;
-  dp.V = V;
-  dp.Vp = L.Vp;
-  dp.Mp = L.Mp;
-  dp.gm = kGroupFwd;
-  dp.idx = at<int>(ws, L.idx);
-  dp.tgt_c = at<int>(ws, L.tgt);
-  dp.row_c = at<int>(ws, L.rowc);
-  dp.hdr = hdr;
-  dp.lse = lse;
-  dp.weight = weight;
-  dp.D = D;
-  dp.DT = DT;
-  RUN("dlogits_gemm", launch_dprod_gemm(dp, persistent_grid(), st));
+  // vocabulary slices: D, D^T for the slice; dHidden partials accumulate
+  // across slices; each slice's dW rows are complete
+  float* dh_part = at<float>(ws, L.dhpart);
+  for (int c = 0; c < L.n_chunks; ++c) {
+    const int v0 = c * L.chunk_tiles * gemm::BN;
+    const int Vc = std::min(V - v0, L.chunk_tiles * gemm::BN);
+    const int Vcp = (int)align_up((size_t)Vc, gemm::BN);
+    DProdArgs dp;
+    dp.hidden = hidden;
+    dp.w = w_vocab + (size_t)v0 * H;
+    dp.hidden_bytes = (unsigned)((size_t)rows * T * H * 2);
+    dp.H = H;
+    dp.V = Vc;
+    dp.Vp = Vcp;
+    dp.Mp = L.Mp;
+    dp.gm = kGroupFwd;
+    dp.idx = at<int>(ws, L.idx);
+    dp.tgt_c = at<int>(ws, L.tgt);
+    dp.row_c = at<int>(ws, L.rowc);
+    dp.hdr = hdr;
+    dp.lse = lse;
+    dp.weight = weight;
+    dp.D = D;
+    dp.DT = DT;
+    RUN("dlogits_gemm", launch_dprod_gemm(dp, persistent_grid(), st));
 
-  DhArgs dh;
-  dh.D = D;
-  dh.wt = WT;
-  dh.H = H;
-  dh.V = V;
-  dh.Vp = L.Vp;
-  dh.Mp = L.Mp;
-  dh.gm = kGroupBwd;
-  dh.splitk = kSplitDh;
-  dh.hdr = hdr;
-  dh.part = at<float>(ws, L.dhpart);
-  RUN("dhidden_gemm", launch_dh_gemm(dh, persistent_grid(), st));
+    DhArgs dh;
+    dh.D = D;
+    dh.wt = WT + v0;
+    dh.H = H;
+    dh.V = Vc;
+    dh.Vp = Vcp;
+    dh.ldw = L.Vp;
+    dh.Mp = L.Mp;
+    dh.gm = kGroupBwd;
+    dh.splitk = kSplitDh;
+    dh.accumulate = c > 0;
+    dh.hdr = hdr;
+    dh.part = dh_part;
+    RUN("dhidden_gemm", launch_dh_gemm(dh, persistent_grid(), st));
+
+    DwArgs dw;
+    dw.DT = DT;
+    dw.ht = HT;
+    dw.V = Vc;
+    dw.H = H;
+    dw.Vp = Vcp;
+    dw.Mp = L.Mp;
+    dw.gm = kGroupBwd;
+    dw.accumulate = accumulate_dw;
+    dw.hdr = hdr;
+    dw.d_w = d_w_vocab + (size_t)v0 * H;
+    RUN("dw_gemm", launch_dw_gemm(dw, persistent_grid(), st));
+  }
+  const int* idx_c = at<int>(ws, L.idx);
+  const int* tgt_c = at<int>(ws, L.tgt);
+  const int* row_c = at<int>(ws, L.rowc);
+
   DhFinishArgs df;
-  df.part = dh.part;
+  df.part = dh_part;
   df.w = w_vocab;
-  df.idx = dp.idx;
-  df.tgt_c = dp.tgt_c;
-  df.row_c = dp.row_c;
+  df.idx = idx_c;
+  df.tgt_c = tgt_c;
+  df.row_c = row_c;
   df.weight = weight;
   df.hdr = hdr;
   df.H = H;
@@ -631,27 +670,14 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
   ZeroRowsArgs z{mask, H, d_hidden};
   RUN("zero_rows", launch_zero_rows(z, (long)rows * T, st));
 
-  DwArgs dw;
-  dw.DT = DT;
-  dw.ht = HT;
-  dw.V = V;
-  dw.H = H;
-  dw.Vp = L.Vp;
-  dw.Mp = L.Mp;
-  dw.gm = kGroupBwd;
-  dw.accumulate = accumulate_dw;
-  dw.hdr = hdr;
-  dw.d_w = d_w_vocab;
-  RUN("dw_gemm", launch_dw_gemm(dw, persistent_grid(), st));
-
   // one-hot term of dW_vocab: sort positions by target, subtract per-target sums
   // (keys span [0, V], V standing for "no target in this slice")
   int bits = 1;
   while (bits < 31 && (1 << bits) <= V) ++bits;
   SortArgs so;
-  so.tgt_c = dp.tgt_c;
-  so.idx = dp.idx;
-  so.row_c = dp.row_c;
+  so.tgt_c = tgt_c;
+  so.idx = idx_c;
+  so.row_c = row_c;
   so.weight = weight;
   so.hdr = hdr;
   so.V = V;

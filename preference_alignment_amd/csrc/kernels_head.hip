@@ -118,13 +118,24 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CompactArgs a) {
 constexpr int kEpiBytes = 8192;  // per-position staging + cross-wave reduction
 
 template <typename F>
-__device__ __forceinline__ void for_vocab(const Acc& acc, int j, bool full, int vbase, int V, int lane, F f) {
+__device__ __forceinline__ void for_vocab(const Acc& acc, int j, F f) {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if (full || vbase + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3) < V) f(acc.c[i][j][e]);
-    }
+    for (int e = 0; e < 16; ++e) f(acc.c[i][j][e]);
+}
+
+// Logits of vocabulary rows past V (the zero-filled rows of the last tile)
+// become -inf, so the epilogues need no per-element bounds test: they drop
+// out of the max, and exp gives 0.  Only the last vocabulary tile takes this.
+__device__ __forceinline__ void mask_vocab_tail(Acc& acc, int vbase, int V, int lane) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (vbase + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3) >= V) acc.c[i][j][e] = -INFINITY;
 }
 
 template <bool ZSUM>
@@ -158,20 +169,21 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
     mainloop(acc, wop, hop, a.H / BK, smem, wave, lane, wm, wn);
 
     const int vbase = n0 + wm * 128;  // first vocabulary row of this wave
-    const bool full = n0 + BN <= a.V;
+    if (n0 + BN > a.V) mask_vocab_tail(acc, vbase, a.V, lane);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int pl = acc_col(wn, j, lane);  // position within the tile
       float mx = -INFINITY;
-      for_vocab(acc, j, full, vbase, a.V, lane, [&](float v) { mx = fmaxf(mx, v); });
+      for_vocab(acc, j, [&](float v) { mx = fmaxf(mx, v); });
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float ml = mx * kLog2e;
+      // a lane pair whose rows are all past V keeps (-inf, 0)
+      const float ml = mx == -INFINITY ? 0.f : mx * kLog2e;
       float s = 0.f;
-      for_vocab(acc, j, full, vbase, a.V, lane, [&](float v) { s += fast_exp2(fmaf(v, kLog2e, -ml)); });
+      for_vocab(acc, j, [&](float v) { s += fast_exp2(fmaf(v, kLog2e, -ml)); });
       s += __shfl_xor(s, 32, 64);
       if (ZSUM) {
         float zs = 0.f;
-        for_vocab(acc, j, full, vbase, a.V, lane, [&](float v) { zs += v; });
+        for_vocab(acc, j, [&](float v) { zs += v == -INFINITY ? 0.f : v; });
         zs += __shfl_xor(zs, 32, 64);
         if (lane < 32) red_z[wm * 256 + pl] = zs;
       }
@@ -180,12 +192,25 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
         const int r = off & 31;
         if (((r >> 2) & 1) == (lane >> 5) && m0 + pl < n_c) {
           const int ii = off >> 5, ee = ((r >> 3) << 2) | (r & 3);
-          float v = 0.f;
+          // acc.c[ii][j][ee] through a select tree on the index bits (6 lane
+          // masks in all, instead of one per candidate element)
+          float vi[FM];
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
+          for (int i = 0; i < FM; ++i) {
+            float t[16];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) v = (ii == i && ee == e) ? acc.c[i][j][e] : v;
-          a.tgt_logit[m0 + pl] = v;
+            for (int e = 0; e < 16; ++e) t[e] = acc.c[i][j][e];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const bool hi = (ee >> b) & 1;
+#pragma unroll
+              for (int k = 0; k < (16 >> (b + 1)); ++k) t[k] = hi ? t[2 * k + 1] : t[2 * k];
+            }
+            vi[i] = t[0];
+          }
+          const float v01 = (ii & 1) ? vi[1] : vi[0];
+          const float v23 = (ii & 1) ? vi[3] : vi[2];
+          a.tgt_logit[m0 + pl] = (ii & 2) ? v23 : v01;
         }
       }
       if (lane < 32) red[wm * 256 + pl] = make_float2(mx, s);
@@ -423,6 +448,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
     }
     Acc acc;
     mainloop(acc, wop, hop, a.H / BK, smem, wave, lane, wm, wn);
+    if (n0 + BN > a.V) mask_vocab_tail(acc, n0 + wm * 128, a.V, lane);
 
     // D values (bf16) into the staging tile; the pipeline LDS is free now
 #pragma unroll
@@ -438,8 +464,8 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
           float d[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const float p = fast_exp2(fmaf(acc.c[i][j][4 * q + u], kLog2e, -L));
-            d[u] = n0 + vl + u < a.V ? wr * p : 0.f;
+            // rows past V hold -inf: exp gives 0
+            d[u] = wr * fast_exp2(fmaf(acc.c[i][j][4 * q + u], kLog2e, -L));
           }
           uint2 pk;
           pk.x = pack_bf16x2(d[0], d[1]);
@@ -506,7 +532,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
       for (int it = 0; it < LOADS_PER_THREAD; ++it) {
         const int r = row_loader_row(it, tid);
         dop.rows[it] = a.D + (size_t)(m0 + r) * a.Vp + (size_t)kb * BK + lchunk * 8;
-        wop.rows[it] = a.wt + (size_t)min(n0 + r, a.H - 1) * a.Vp + (size_t)kb * BK + lchunk * 8;
+        wop.rows[it] = a.wt + (size_t)min(n0 + r, a.H - 1) * a.ldw + (size_t)kb * BK + lchunk * 8;
       }
     }
     Acc acc;
@@ -522,7 +548,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = n0 + acc_col(wn, j, lane);
-          if (col < a.H) dst[col] = acc.c[i][j][e];
+          if (col < a.H) dst[col] = a.accumulate ? dst[col] + acc.c[i][j][e] : acc.c[i][j][e];
         }
       }
     }

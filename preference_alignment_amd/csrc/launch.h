@@ -123,9 +123,10 @@ struct DProdArgs {
 };
 
 struct DhArgs {
-  const uint16_t* D;
-  const uint16_t* wt;   // [H, Vp]
-  int H, V, Vp, Mp, gm, splitk;
+  const uint16_t* D;    // [Mp, Vp] the slice's D
+  const uint16_t* wt;   // [H, ldw] W^T, offset to the slice's first vocabulary column
+  int H, V, Vp, ldw, Mp, gm, splitk;
+  int accumulate;       // add to the partials (later vocabulary slices)
   const WsHeader* hdr;
   float* part;  // [splitk, Mp, H] fp32 partial sums
 };
