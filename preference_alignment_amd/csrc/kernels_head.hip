@@ -480,22 +480,33 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
       const int g = it * NTHREADS + tid;
       const int p = g >> 5, c = g & 31;
       const u32x4 v = *(const u32x4*)(smem + stage_off(p, c * 8));
-      *(u32x4*)(a.D + (size_t)(m0 + p) * a.Vp + n0 + c * 8) = v;
+      __builtin_nontemporal_store(v, (u32x4*)(a.D + (size_t)(m0 + p) * a.Vp + n0 + c * 8));
     }
-    // D^T rows: vocabulary n0+v, positions m0 .. m0+255
+    // D^T rows: vocabulary n0+v, positions m0 .. m0+255, through transposing
+    // LDS reads.  In a 16-lane group, lane L supplies the 8-byte piece
+    // (vocabulary 4*c0 .. +3) of position row P0 + 8*(L&3) + (L>>2); the read
+    // hands lane i the entries of vocabulary 4*c0 + (i&3) at positions
+    // P0 + 8*(i>>2) + 0..3.  A second read 4 rows down gives the next 4
+    // positions, so each lane ends with 8 consecutive positions (16 bytes).
+    {
+      const int grp = lane >> 4, L = lane & 15;
 #pragma unroll 2
-    for (int it = 0; it < BN * 32 / NTHREADS; ++it) {
-      const int g = it * NTHREADS + tid;
-      const int v = g >> 5, c = g & 31;
-      uint32_t w4[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t lo = *(const uint16_t*)(smem + stage_off(c * 8 + 2 * u, v));
-        const uint32_t hi = *(const uint16_t*)(smem + stage_off(c * 8 + 2 * u + 1, v));
-        w4[u] = lo | (hi << 16);
+      for (int it = 0; it < BN * BM / (8 * NTHREADS); ++it) {
+        const int u = it * (NTHREADS / 64) + wave;  // 0 .. 127
+        const int c0 = u & 63;                      // vocabulary quad
+        const int P0 = (u >> 6) * 128 + 32 * grp;   // first position of this lane group
+        const int prow = P0 + 8 * (L & 3) + (L >> 2);
+        typedef __attribute__((address_space(3))) i16x4_t* lds_q;
+        const i16x4_t A = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_q)(smem + stage_off(prow, 4 * c0)));
+        const i16x4_t B = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_q)(smem + stage_off(prow + 4, 4 * c0)));
+        const int v = 4 * c0 + (L & 3);
+        const int P = P0 + 8 * (L >> 2);
+        const u32x4 o = {(uint32_t)(uint16_t)A[0] | ((uint32_t)(uint16_t)A[1] << 16),
+                         (uint32_t)(uint16_t)A[2] | ((uint32_t)(uint16_t)A[3] << 16),
+                         (uint32_t)(uint16_t)B[0] | ((uint32_t)(uint16_t)B[1] << 16),
+                         (uint32_t)(uint16_t)B[2] | ((uint32_t)(uint16_t)B[3] << 16)};
+        __builtin_nontemporal_store(o, (u32x4*)(a.DT + (size_t)(n0 + v) * a.Mp + m0 + P));
       }
-      const u32x4 o = {w4[0], w4[1], w4[2], w4[3]};
-      *(u32x4*)(a.DT + (size_t)(n0 + v) * a.Mp + m0 + c * 8) = o;
     }
     __syncthreads();
   }
