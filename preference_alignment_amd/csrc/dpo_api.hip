@@ -112,7 +112,8 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     L.valsA = take((size_t)L.Mp * 4);
     L.keysB = take((size_t)L.Mp * 4);
     L.valsB = take((size_t)L.Mp * 4);
-    L.dhpart = take((size_t)kSplitDh * L.Mp * H * 4);
+    // one fp32 partial per (vocabulary slice, K split): written once, summed by the finish
+    L.dhpart = take((size_t)L.n_chunks * kSplitDh * L.Mp * H * 4);
     L.spos = take((size_t)L.Mp * 4);
     L.sw = take((size_t)L.Mp * 4);
     L.ohcont = take((size_t)(L.Mp / 64) * H * 4);
@@ -595,8 +596,9 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
   GatherHTArgs gh{hidden, at<int>(ws, L.idx), hdr, H, L.Mp, HT};
   RUN("gather_ht", launch_gather_ht(gh, st));
 
-  // vocabulary slices: D, D^T for the slice; dHidden partials accumulate
-  // across slices; each slice's dW rows are complete
+  // vocabulary slices: D, D^T for the slice; each slice writes its own
+  // dHidden partials (the finish adds them in a fixed order); each slice's dW
+  // rows are complete
   float* dh_part = at<float>(ws, L.dhpart);
   for (int c = 0; c < L.n_chunks; ++c) {
     const int v0 = c * L.chunk_tiles * gemm::BN;
@@ -631,9 +633,8 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
     dh.Mp = L.Mp;
     dh.gm = kGroupBwd;
     dh.splitk = kSplitDh;
-    dh.accumulate = c > 0;
     dh.hdr = hdr;
-    dh.part = dh_part;
+    dh.part = dh_part + (size_t)c * kSplitDh * L.Mp * H;
     RUN("dhidden_gemm", launch_dh_gemm(dh, persistent_grid(), st));
 
     DwArgs dw;
@@ -663,7 +664,7 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
   df.hdr = hdr;
   df.H = H;
   df.Mp = L.Mp;
-  df.splitk = kSplitDh;
+  df.splitk = L.n_chunks * kSplitDh;
   df.d_hidden = d_hidden;
   RUN("dhidden_finish", launch_dh_finish(df, L.Mp, st));
 

@@ -126,7 +126,6 @@ struct DhArgs {
   const uint16_t* D;    // [Mp, Vp] the slice's D
   const uint16_t* wt;   // [H, ldw] W^T, offset to the slice's first vocabulary column
   int H, V, Vp, ldw, Mp, gm, splitk;
-  int accumulate;       // add to the partials (later vocabulary slices)
   const WsHeader* hdr;
   float* part;  // [splitk, Mp, H] fp32 partial sums
 };
@@ -139,7 +138,7 @@ struct DhFinishArgs {
   const int* row_c;
   const float* weight;  // [rows]
   const WsHeader* hdr;
-  int H, Mp, splitk;
+  int H, Mp, splitk;  // splitk: number of [Mp, H] partial slots to add
   float* d_hidden;  // [rows*T, H]
 };
 
