@@ -125,6 +125,14 @@ __device__ __forceinline__ void for_vocab(const Acc& acc, int j, F f) {
     for (int e = 0; e < 16; ++e) f(acc.c[i][j][e]);
 }
 
+// The lane / thread index through an empty asm: offsets computed from it in an
+// epilogue cannot be hoisted out of the persistent tile loop, where they would
+// stay live across the main loop and push it into register spills.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Logits of vocabulary rows past V (the zero-filled rows of the last tile)
 // become -inf, so the epilogues need no per-element bounds test: they drop
 // out of the max, and exp gives 0.  Only the last vocabulary tile takes this.
@@ -451,16 +459,17 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
     if (n0 + BN > a.V) mask_vocab_tail(acc, n0 + wm * 128, a.V, lane);
 
     // D values (bf16) into the staging tile; the pipeline LDS is free now
+    const int elane = opaque(lane), etid = opaque(tid);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int pl = acc_col(wn, j, lane);
+      const int pl = acc_col(wn, j, elane);
       const float L = lse_s[pl];
       const float wr = w_s[pl];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int vl = wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);  // first of 4 vocabulary rows
+          const int vl = wm * 128 + i * 32 + 8 * q + 4 * (elane >> 5);  // first of 4 vocabulary rows
           float d[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -477,7 +486,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
     // D rows: position m0+p, vocabulary n0 .. n0+255
 #pragma unroll 4
     for (int it = 0; it < BM * 32 / NTHREADS; ++it) {
-      const int g = it * NTHREADS + tid;
+      const int g = it * NTHREADS + etid;
       const int p = g >> 5, c = g & 31;
       const u32x4 v = *(const u32x4*)(smem + stage_off(p, c * 8));
       __builtin_nontemporal_store(v, (u32x4*)(a.D + (size_t)(m0 + p) * a.Vp + n0 + c * 8));
@@ -489,7 +498,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
     // P0 + 8*(i>>2) + 0..3.  A second read 4 rows down gives the next 4
     // positions, so each lane ends with 8 consecutive positions (16 bytes).
     {
-      const int grp = lane >> 4, L = lane & 15;
+      const int grp = elane >> 4, L = elane & 15;
 #pragma unroll 2
       for (int it = 0; it < BN * BM / (8 * NTHREADS); ++it) {
         const int u = it * (NTHREADS / 64) + wave;  // 0 .. 127
