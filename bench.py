@@ -413,22 +413,30 @@ def main():
                 "traffic": measured_traffic(dom, label), "avg_ms": avg,
                 "algorithmic_bytes_per_launch": per_kernel_bytes[dom]}
         step_bytes = n_c * V * eb * 2 + E * eb
-        extra = {"step_hbm_frac": step_bytes / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS}
+        extra = {"step_hbm_frac": step_bytes / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS,
+                 "kernels_ms_per_step": {k: round(v[0] / a.steps, 4) for k, v in kernels.items()}}
     else:
         gemms = ["fwd_gemm"] if a.workload == 3 else ["fwd_gemm", "dlogits_gemm", "dhidden_gemm", "dw_gemm"]
         Vw = runner.Vs if row == "vocab-shard" else V
-        flops = 2.0 * n_c * H * Vw
-        dom = max(gemms, key=lambda k: kern_avg.get(k, (0,))[0]) if kern_avg else gemms[0]
+        flops_step = 2.0 * n_c * H * Vw   # each contraction, per step
+        # the backward contractions run once per vocabulary slice: the dominant
+        # one is the one with the most time per step, and its algorithmic flops
+        # per launch are its per-step flops over its launches per step
+        tot = {k: kernels[k][0] for k in gemms if k in kernels}
+        dom = max(tot, key=tot.get) if tot else gemms[0]
         avg = kern_avg[dom][0] if dom in kern_avg else None
+        launches = kernels[dom][1] / a.steps if dom in kernels else 1.0
+        flops = flops_step / launches
         ach = flops / (avg / 1e3) / 1e12 if avg else None
         roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS if ach else None,
                 "traffic": measured_traffic(dom, label), "avg_ms": avg,
                 "algorithmic_flops_per_launch": flops}
-        step_flops = flops * len(gemms)
+        step_flops = flops_step * len(gemms)
         extra = {"step_mfma_frac": step_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-                 "step_useful_mfma_frac": (flops * (1 if a.workload == 3 else 3)) / (ms_step / 1e3) / 1e12
-                 / PEAK_BF16_TFLOPS}
+                 "step_useful_mfma_frac": (flops_step * (1 if a.workload == 3 else 3)) / (ms_step / 1e3) / 1e12
+                 / PEAK_BF16_TFLOPS,
+                 "kernels_ms_per_step": {k: round(v[0] / a.steps, 4) for k, v in kernels.items()}}
 
     cpu = None
     if not a.no_cpu_baseline:

@@ -37,9 +37,14 @@ def test_workspace_sizes(L):
     # logits ops ignore H
     assert D.dpo_workspace_bytes(D.DPO_OP_LOGITS_SEQ_LOGPS, 8, 2048, 0, 128256) > 0
     assert D.dpo_workspace_bytes(D.DPO_OP_LOGITS_BACKWARD, 8, 2048, 0, 128256) == 256
-    # the backward holds the bf16 softmax part of dlogits in both layouts: >= 2 * 2 * (rows*T) * V bytes
+    # the backward holds the bf16 softmax part of dlogits in both layouts for one
+    # vocabulary slice at a time: each copy near (and under) 1 GiB here, never the
+    # whole [positions x V] tensor
     bw = D.dpo_workspace_bytes(D.DPO_OP_HEAD_BACKWARD, 8, 2048, 4096, 128256)
-    assert bw >= 4 * 8 * 2048 * 128256
+    assert bw < 2 * 2 * 8 * 2048 * 128256
+    assert bw > 2 * 0.9 * 2 ** 30
+    small = D.dpo_workspace_bytes(D.DPO_OP_HEAD_BACKWARD, 4, 64, 256, 1024)
+    assert small >= 2 * 2 * 256 * 1024   # one slice holds the whole (small) vocabulary
     # more rows never need less
     assert D.dpo_workspace_bytes(0, 16, 2048, 4096, 128256) > ok
 

@@ -31,6 +31,10 @@ CASES = {
                                    w_std=0.05, layout=W.PAIRS_HALVES),
     # peaked softmax (logit std ~3): the softmax term of the gradient is large
     "peaked": lambda: _case("peaked", seed=103, w_std=0.1875),
+    # 16,384 positions x V = 40,000: the backward runs in two vocabulary slices
+    # (the slice holding D stays under 1 GiB), the second one ragged
+    "two_vocab_slices": lambda: _case("two_vocab_slices", seed=105, rows=8, T=2048, H=64, V=40000,
+                                      prompt_lo=16, prompt_hi=64, w_std=0.25, targets_dist="zipf"),
     # minimum sizes
     "tiny_min": lambda: _case("tiny_min", seed=104, rows=2, T=3, H=64, V=8, prompt_lo=0, prompt_hi=1,
                               w_std=0.3),
@@ -118,9 +122,10 @@ def test_empty_rows_and_empty_batch():
     assert torch.equal(dw2, prev)
 
 
-def test_accumulate_dw_adds():
+@pytest.mark.parametrize("case", ["ragged_small", "two_vocab_slices"])
+def test_accumulate_dw_adds(case):
     dev = need_gpu()
-    x = CASES["ragged_small"]()
+    x = CASES[case]()
     d = dev_inputs(x, dev)
     g = run_forward(x, d, dev)
     weight = torch.linspace(-0.05, 0.05, x.rows, dtype=torch.float32, device=dev)
@@ -131,9 +136,10 @@ def test_accumulate_dw_adds():
     assert float((dw2 - 2 * dw1).abs().max()) <= 1e-6 * float(dw1.abs().max())
 
 
-def test_run_to_run_bitwise_deterministic():
+@pytest.mark.parametrize("case", ["ragged_medium", "two_vocab_slices"])
+def test_run_to_run_bitwise_deterministic(case):
     dev = need_gpu()
-    x = CASES["ragged_medium"]()
+    x = CASES[case]()
     d = dev_inputs(x, dev)
     outs = []
     for _ in range(2):
