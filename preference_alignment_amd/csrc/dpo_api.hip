@@ -29,6 +29,7 @@ constexpr int kSplitDh = 2;
 // slice of the vocabulary at a time: each of D and D^T stays under this many
 // bytes (balanced slices of whole 256-wide tiles).
 constexpr size_t kChunkBytes = size_t(1) << 30;
+constexpr int kTransPad = 64;  // elements
 
 // ---------------------------------------------------------------------------
 // workspace layout
@@ -39,6 +40,7 @@ struct Layout {
   int nVt = 0;  // vocabulary tiles of the forward contraction
   int chunk_tiles = 0;  // vocabulary tiles per backward slice
   int n_chunks = 0;
+  int ldt = 0;  // row stride (elements) of D^T and Hc^T: positions plus a pad
   size_t hdr = 0, idx = 0, tgt = 0, rowc = 0, rowoff = 0;
   size_t part = 0, tlogit = 0, lse64 = 0, logp64 = 0, partz = 0, zsum64 = 0;
   size_t D = 0, DT = 0, WT = 0, HT = 0;
@@ -104,10 +106,14 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     L.n_chunks = cdiv(L.nVt, max_tiles);
     L.chunk_tiles = cdiv(L.nVt, L.n_chunks);
     const size_t Vcp = (size_t)L.chunk_tiles * gemm::BN;
+    // D^T and Hc^T rows are positions long; a pad of 128 bytes keeps their
+    // stride off a power of two (2^15 bytes at 16,384 positions), where all
+    // rows of a tile would fall on the same HBM channels
+    L.ldt = L.Mp + kTransPad;
     L.D = take((size_t)L.Mp * Vcp * 2);
-    L.DT = take(Vcp * L.Mp * 2);
+    L.DT = take(Vcp * L.ldt * 2);
     L.WT = take((size_t)H * L.Vp * 2);
-    L.HT = take((size_t)H * L.Mp * 2);
+    L.HT = take((size_t)H * L.ldt * 2);
     L.keysA = take((size_t)L.Mp * 4);
     L.valsA = take((size_t)L.Mp * 4);
     L.keysB = take((size_t)L.Mp * 4);
@@ -593,7 +599,7 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
 
   TransposeWArgs tw{w_vocab, V, H, L.Vp, WT};
   RUN("transpose_w", launch_transpose_w(tw, st));
-  GatherHTArgs gh{hidden, at<int>(ws, L.idx), hdr, H, L.Mp, HT};
+  GatherHTArgs gh{hidden, at<int>(ws, L.idx), hdr, H, L.Mp, L.ldt, HT};
   RUN("gather_ht", launch_gather_ht(gh, st));
 
   // vocabulary slices: D, D^T for the slice; each slice writes its own
@@ -621,6 +627,7 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
     dp.weight = weight;
     dp.D = D;
     dp.DT = DT;
+    dp.ldt = L.ldt;
     RUN("dlogits_gemm", launch_dprod_gemm(dp, persistent_grid(), st));
 
     DhArgs dh;
@@ -644,6 +651,7 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
     dw.H = H;
     dw.Vp = Vcp;
     dw.Mp = L.Mp;
+    dw.ldt = L.ldt;
     dw.gm = kGroupBwd;
     dw.accumulate = accumulate_dw;
     dw.hdr = hdr;

@@ -405,7 +405,7 @@ __global__ __launch_bounds__(256) void k_gather_ht(GatherHTArgs a) {
     tile[r][tx] = m < n_c ? a.hidden[(size_t)a.idx[m] * a.H + h0 + tx] : (uint16_t)0;
   }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) a.ht[(size_t)(h0 + r) * a.Mp + m0 + tx] = tile[tx][r];
+  for (int r = ty; r < 64; r += 4) a.ht[(size_t)(h0 + r) * a.ldt + m0 + tx] = tile[tx][r];
 }
 
 // ---------------------------------------------------------------------------
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
                          (uint32_t)(uint16_t)A[2] | ((uint32_t)(uint16_t)A[3] << 16),
                          (uint32_t)(uint16_t)B[0] | ((uint32_t)(uint16_t)B[1] << 16),
                          (uint32_t)(uint16_t)B[2] | ((uint32_t)(uint16_t)B[3] << 16)};
-        __builtin_nontemporal_store(o, (u32x4*)(a.DT + (size_t)(n0 + v) * a.Mp + m0 + P));
+        __builtin_nontemporal_store(o, (u32x4*)(a.DT + (size_t)(n0 + v) * a.ldt + m0 + P));
       }
     }
     __syncthreads();
@@ -619,8 +619,8 @@ __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
     int mt, nt;
     sc.coords(t, mt, nt);
     const int m0 = mt * BM, n0 = nt * BN;
-    const RowOperand dop = row_operand(a.DT + (size_t)m0 * a.Mp, a.Mp, (long)a.Vp - m0, 0, tid);
-    const RowOperand hop = row_operand(a.ht + (size_t)n0 * a.Mp, a.Mp, (long)a.H - n0, 0, tid);
+    const RowOperand dop = row_operand(a.DT + (size_t)m0 * a.ldt, a.ldt, (long)a.Vp - m0, 0, tid);
+    const RowOperand hop = row_operand(a.ht + (size_t)n0 * a.ldt, a.ldt, (long)a.H - n0, 0, tid);
     Acc acc;
     mainloop(acc, dop, hop, nk, smem, wave, lane, wm, wn);
 #pragma unroll

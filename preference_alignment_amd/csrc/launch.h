@@ -103,8 +103,8 @@ struct GatherHTArgs {
   const uint16_t* hidden;
   const int* idx;
   const WsHeader* hdr;
-  int H, Mp;
-  uint16_t* ht;  // [H, Mp]
+  int H, Mp, ldt;
+  uint16_t* ht;  // [H, ldt]: row h holds the completion positions' h-th entries
 };
 
 struct DProdArgs {
@@ -119,7 +119,8 @@ struct DProdArgs {
   const float* lse;     // [rows*T] from the forward
   const float* weight;  // [rows]
   uint16_t* D;          // [Mp, Vp] bf16
-  uint16_t* DT;         // [Vp, Mp] bf16
+  uint16_t* DT;         // [Vp, ldt] bf16
+  int ldt;              // row stride of D^T (positions, padded)
 };
 
 struct DhArgs {
@@ -171,9 +172,9 @@ struct OnehotDwArgs {
 };
 
 struct DwArgs {
-  const uint16_t* DT;   // [Vp, Mp]
-  const uint16_t* ht;   // [H, Mp]
-  int V, H, Vp, Mp, gm, accumulate;
+  const uint16_t* DT;   // [Vp, ldt]
+  const uint16_t* ht;   // [H, ldt]
+  int V, H, Vp, Mp, ldt, gm, accumulate;
   const WsHeader* hdr;
   float* d_w;  // [V, H]
 };
