@@ -1,24 +1,26 @@
 // bf16 MFMA main loop shared by the four LM-head contractions (gfx950).
 //
-// C[i][j] = sum_k R[i][k] * C[k][j] with each operand either K-contiguous
-// (ROW layout) or contiguous along its MFMA dimension (TR layout).  The
-// kernels that use this core differ in their operands and epilogues:
-//   forward / recompute : R = W_vocab rows (ROW), C = hidden rows at completion positions (ROW)
-//   dHidden             : R = D rows (ROW),       C = W_vocab (TR: K = vocabulary rows)
-//   dW_vocab            : R = D (TR: K = positions), C = gathered hidden (TR)
+// C[i][j] = sum_k R[i][k] * C[j][k]: both operands are K-contiguous in memory.
+// The kernels that use this core differ in their operands and epilogues:
+//   forward / recompute : R = W_vocab rows, C = hidden rows at completion positions
+//   dHidden             : R = D rows (K = vocabulary), C = W_vocab^T rows
+//   dW_vocab            : R = D^T rows (K = positions), C = gathered hidden^T rows
+// (the backward writes D^T and W^T so that every operand is K-contiguous: an
+// LDS-transposed read of D for dW_vocab measured 40 % slower).
 //
 // Block tile 256x256x64, 512 threads = 8 waves in a 2x4 grid (two waves per
 // SIMD, so one wave's LDS and barrier waits are covered by the other's MFMAs);
 // each wave owns a 128x64 sub-tile held as 4x2 fragments of
 // v_mfma_f32_32x32x16_bf16 (128 accumulator registers).  Operand tiles go
-// from global memory straight into LDS with global_load_lds_dwordx4 (16 bytes
-// per lane, no register staging), double buffered (2 stages x 2 operands x
+// from global memory straight into LDS with buffer_load_dwordx4 ... lds
+// (global_load_lds_dwordx4 for dHidden; 16 bytes per lane, no register
+// staging), double buffered (2 stages x 2 operands x
 // 32 KiB = 128 KiB of the 160 KiB LDS).  The K loop is software pipelined:
 // the fragments of the next 16-wide K step are read while the MFMAs of the
 // current one issue, and the stage barrier sits inside the MFMA stream of the
 // last step of a stage, with the next stage's first fragments read across it.
 //
-// global_load_lds places lane L's 16 bytes at (wave base + 16 L), so the LDS
+// Both loads place lane L's 16 bytes at (wave base + 16 L), so the LDS
 // swizzles below are realised by choosing which global chunk each lane fetches.
 //
 // MFMA 32x32x16 register layout (CDNA3/CDNA4 32x32 family): lane l supplies
@@ -54,19 +56,10 @@ struct Acc {
   floatx16 c[FM][FN];
 };
 
-// Operand tiles come in two LDS layouts.
-//
-// ROW: the operand is K-contiguous in memory (rows of the MFMA dimension,
-// 64 K values each).  Tile = 256 rows x 128 bytes; the 16-byte chunk c of row
-// r sits at chunk c ^ ((r >> 1) & 7).  Fragments are single ds_read_b128.
-//
-// TR: the operand is contiguous along the MFMA dimension (rows = K).  Tile =
-// 64 K rows x 512 bytes (256 values); the 16-byte chunk c of K row r sits at
-// chunk c ^ 4 (r & 3), so the 4 rows x 2 chunks that each 16-lane group reads
-// land in distinct banks, and the two groups of a half-wave in disjoint ones.  Fragments come from two ds_read_b64_tr_b16 (gfx950
-// transposing LDS read): in each group of 16 lanes, lane L addresses K row
-// (L / 4) and columns 4 (L % 4) .. +3 of a 4 x 16 block, and lane i receives
-// the 4 K values of column i, which is the MFMA operand layout.
+// LDS layout of an operand tile (rows of the MFMA dimension, 64 K values
+// each): 256 rows x 128 bytes; the 16-byte chunk c of row r sits at chunk
+// c ^ ((r >> 1) & 7).  Fragments are single ds_read_b128.
+
 // ROW operands are read with buffer_load_dwordx4 ... lds: one uniform buffer
 // descriptor, a 32-bit byte offset per lane and loaded row (fixed for the
 // tile), and the K step in the scalar offset.  Offsets at or beyond the
@@ -93,19 +86,8 @@ __device__ __forceinline__ RowOperand row_operand(const uint16_t* base, size_t l
     op.voff[it] = (unsigned)(((size_t)(it * LOADER_ROW_STRIDE + (tid >> 3)) * ld + k0 + lchunk * 8) * 2);
   return op;
 }
-struct TrOperand {
-  const uint16_t* base;  // element (K row 0, column 0) of the operand
-  size_t ld;             // elements between K rows
-  int col;               // this thread's column: tile column 0 + lchunk * 8 (clamped)
-  int row0;              // first K row of the loop
-  int rmax;              // last valid K row (rows beyond are clamped to it)
-  int kr0;               // this thread's first tile row
-};
-
 __device__ __forceinline__ int row_lchunk(int tid) { return (tid & 7) ^ ((tid >> 4) & 7); }
 __device__ __forceinline__ int row_loader_row(int it, int tid) { return it * LOADER_ROW_STRIDE + (tid >> 3); }
-__device__ __forceinline__ int tr_lchunk(int tid) { return (tid & 31) ^ (((tid >> 5) & 3) << 2); }
-__device__ __forceinline__ int tr_loader_row(int it, int tid) { return it * 16 + (tid >> 5); }
 
 // ROW operand read with global_load_lds from per-row 64-bit pointers.  Same
 // LDS layout as RowOperand; measured faster than buffer loads for the
@@ -130,15 +112,6 @@ __device__ __forceinline__ void load_stage(const RowOperand& op, int kstep, char
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, dst, 16, op.voff[it], soff, 0, 0);
   }
 }
-__device__ __forceinline__ void load_stage(const TrOperand& op, int kstep, char* lds_tile, int wave) {
-#pragma unroll
-  for (int it = 0; it < LOADS_PER_THREAD; ++it) {
-    lds_ptr_t dst = (lds_ptr_t)(lds_tile + (it * NTHREADS + wave * 64) * 16);
-    const int r = min(op.row0 + kstep * BK + op.kr0 + it * 16, op.rmax);
-    __builtin_amdgcn_global_load_lds((const void*)(op.base + (size_t)r * op.ld + op.col), dst, 16, 0, 0);
-  }
-}
-
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -157,36 +130,10 @@ struct RowFrag {
     return *(const bf16x8_t*)(tile + off[kk] + f * 4096);
   }
 };
-template <int NF>
-struct TrFrag {
-  // byte offset of the two 4-row reads (h = 0, 1) of fragment f at K step 0;
-  // K step kk adds kk * 16 rows = kk * 8192 bytes (the swizzle depends only on
-  // the K row modulo 4, which a step of 16 rows leaves unchanged)
-  int off[NF][2];
-  __device__ __forceinline__ void init(int base, int lane) {
-    const int q = lane >> 4, i = lane & 15;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int col = base + 32 * f + 16 * (q & 1) + 4 * (i & 3);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kr = 8 * (q >> 1) + (i >> 2) + 4 * h;
-        off[f][h] = kr * 512 + (((col >> 3) ^ ((kr & 3) << 2)) << 4) + ((col & 7) << 1);
-      }
-    }
-  }
-  __device__ __forceinline__ bf16x8_t read(const char* tile, int f, int kk) const {
-    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tile + off[f][0] + kk * 8192));
-    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tile + off[f][1] + kk * 8192));
-    const short __attribute__((ext_vector_type(8))) v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8_t, v);
-  }
-};
 
 template <typename Op, int NF> struct FragOf;
 template <int NF> struct FragOf<RowOperand, NF> { typedef RowFrag type; };
 template <int NF> struct FragOf<FlatRowOperand, NF> { typedef RowFrag type; };
-template <int NF> struct FragOf<TrOperand, NF> { typedef TrFrag<NF> type; };
 
 // The K loop over nk steps of BK.  nk may be 0 (accumulators stay zero).  The
 // R operand supplies the MFMA rows (wave (wm, wn) owns rows wm*128 .. +128),
