@@ -25,6 +25,10 @@ constexpr int kGroupBwd = 4;
 // The dHidden contraction has few output tiles (positions x H); splitting its
 // K = vocabulary range in two keeps every CU busy through the last round.
 constexpr int kSplitDh = 2;
+// dHidden partial slots are kept for at most this many vocabulary slices;
+// later slices add into slot (slice % kSlotSlices), so the workspace stays
+// linear in the positions when a long batch needs many slices.
+constexpr int kSlotSlices = 4;
 // The backward holds the bf16 softmax part of dlogits (D and D^T) only for one
 // slice of the vocabulary at a time: each of D and D^T stays under this many
 // bytes (balanced slices of whole 256-wide tiles).
@@ -119,7 +123,7 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     L.keysB = take((size_t)L.Mp * 4);
     L.valsB = take((size_t)L.Mp * 4);
     // one fp32 partial per (vocabulary slice, K split): written once, summed by the finish
-    L.dhpart = take((size_t)L.n_chunks * kSplitDh * L.Mp * H * 4);
+    L.dhpart = take((size_t)std::min(L.n_chunks, kSlotSlices) * kSplitDh * L.Mp * H * 4);
     L.spos = take((size_t)L.Mp * 4);
     L.sw = take((size_t)L.Mp * 4);
     L.ohcont = take((size_t)(L.Mp / 64) * H * 4);
@@ -641,7 +645,8 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
     dh.gm = kGroupBwd;
     dh.splitk = kSplitDh;
     dh.hdr = hdr;
-    dh.part = dh_part + (size_t)c * kSplitDh * L.Mp * H;
+    dh.part = dh_part + (size_t)(c % kSlotSlices) * kSplitDh * L.Mp * H;
+    dh.accumulate = c >= kSlotSlices;
     RUN("dhidden_gemm", launch_dh_gemm(dh, persistent_grid(), st));
 
     DwArgs dw;
@@ -672,7 +677,7 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
   df.hdr = hdr;
   df.H = H;
   df.Mp = L.Mp;
-  df.splitk = L.n_chunks * kSplitDh;
+  df.splitk = std::min(L.n_chunks, kSlotSlices) * kSplitDh;
   df.d_hidden = d_hidden;
   RUN("dhidden_finish", launch_dh_finish(df, L.Mp, st));
 

@@ -568,7 +568,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = n0 + acc_col(wn, j, lane);
-          if (col < a.H) dst[col] = acc.c[i][j][e];
+          if (col < a.H) dst[col] = a.accumulate ? dst[col] + acc.c[i][j][e] : acc.c[i][j][e];
         }
       }
     }

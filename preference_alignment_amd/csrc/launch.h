@@ -127,6 +127,7 @@ struct DhArgs {
   const uint16_t* D;    // [Mp, Vp] the slice's D
   const uint16_t* wt;   // [H, ldw] W^T, offset to the slice's first vocabulary column
   int H, V, Vp, ldw, Mp, gm, splitk;
+  int accumulate;  // add into the partials (slices beyond the slot count)
   const WsHeader* hdr;
   float* part;  // [splitk, Mp, H] fp32 partial sums
 };

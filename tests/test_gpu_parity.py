@@ -35,6 +35,10 @@ CASES = {
     # (the slice holding D stays under 1 GiB), the second one ragged
     "two_vocab_slices": lambda: _case("two_vocab_slices", seed=105, rows=8, T=2048, H=64, V=40000,
                                       prompt_lo=16, prompt_hi=64, w_std=0.25, targets_dist="zipf"),
+    # 32,768 position slots x V = 90,000: six vocabulary slices, so slices 5 and
+    # 6 add into the dHidden partial slots of slices 1 and 2
+    "six_vocab_slices": lambda: _case("six_vocab_slices", seed=106, rows=8, T=4096, H=64, V=90000,
+                                      prompt_lo=3400, prompt_hi=3600, w_std=0.25, targets_dist="zipf"),
     # minimum sizes
     "tiny_min": lambda: _case("tiny_min", seed=104, rows=2, T=3, H=64, V=8, prompt_lo=0, prompt_hi=1,
                               w_std=0.3),
