@@ -32,6 +32,8 @@
 // in dHidden.  It is applied exactly in fp32 instead, by a gather of W[y] in
 // the dHidden epilogue and a fixed-order per-target sum for dW_vocab.
 //   k_zero_rows      dHidden = 0 at positions outside the completion mask
+#include <mutex>
+
 #include "dpo_common.h"
 #include "gemm_core.h"
 #include "launch.h"
@@ -854,8 +856,27 @@ __global__ __launch_bounds__(256) void k_zero_rows(ZeroRowsArgs a) {
 // ---------------------------------------------------------------------------
 static int gemm_lds_bytes() { return PIPE_BYTES + kEpiBytes; }
 
+// The 136 KiB of dynamic LDS needs an opt-in per kernel.  It is set once per
+// (kernel, device), on the first launch from a thread whose current device
+// is that device.
 static hipError_t prep_gemm(const void* fn) {
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes());
+  constexpr int kMaxDev = 64, kMaxFn = 8;
+  static std::mutex mu;
+  static const void* fns[kMaxFn] = {};
+  static bool done[kMaxFn][kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  int slot = 0;
+  while (slot < kMaxFn && fns[slot] && fns[slot] != fn) ++slot;
+  if (slot == kMaxFn) return hipErrorUnknown;
+  fns[slot] = fn;
+  if (done[slot][dev]) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes());
+  if (e == hipSuccess) done[slot][dev] = true;
+  return e;
 }
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
@@ -864,10 +885,8 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fwd_gemm(const FwdArgs& a, int grid, hipStream_t s) {
-  static hipError_t once = prep_gemm((const void*)k_fwd_gemm<false>);
-  static hipError_t once_z = prep_gemm((const void*)k_fwd_gemm<true>);
-  if (once != hipSuccess) return once;
-  if (once_z != hipSuccess) return once_z;
+  const hipError_t e = prep_gemm(a.part_z ? (const void*)k_fwd_gemm<true> : (const void*)k_fwd_gemm<false>);
+  if (e != hipSuccess) return e;
   if (a.part_z)
     hipLaunchKernelGGL(k_fwd_gemm<true>, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
   else
@@ -906,8 +925,8 @@ hipError_t launch_gather_ht(const GatherHTArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_dprod_gemm(const DProdArgs& a, int grid, hipStream_t s) {
-  static hipError_t once = prep_gemm((const void*)k_dprod_gemm);
-  if (once != hipSuccess) return once;
+  const hipError_t e = prep_gemm((const void*)k_dprod_gemm);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_dprod_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
   return hipGetLastError();
 }
@@ -918,15 +937,15 @@ hipError_t launch_dh_finish(const DhFinishArgs& a, int Mp, hipStream_t s) {
 }
 
 hipError_t launch_dh_gemm(const DhArgs& a, int grid, hipStream_t s) {
-  static hipError_t once = prep_gemm((const void*)k_dh_gemm);
-  if (once != hipSuccess) return once;
+  const hipError_t e = prep_gemm((const void*)k_dh_gemm);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_dh_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dw_gemm(const DwArgs& a, int grid, hipStream_t s) {
-  static hipError_t once = prep_gemm((const void*)k_dw_gemm);
-  if (once != hipSuccess) return once;
+  const hipError_t e = prep_gemm((const void*)k_dw_gemm);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_dw_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
   return hipGetLastError();
 }
