@@ -108,7 +108,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=256)
+    p.add_argument("--cpu-sample-tokens", type=int, default=None,
+                   help="completion positions per sampled row for the CPU baseline (0 = all); "
+                        "default 1024 for the fused head, all for given logits")
+    p.add_argument("--cpu-sample-pairs", type=int, default=None,
+                   help="pairs in the CPU baseline sample; default 1 for the fused head, all for given logits")
     p.add_argument("--no-kernel-timing", action="store_true")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
     p.add_argument("--row", default="main", choices=ROWS,
@@ -267,33 +271,36 @@ class ShardStep:
                                   self.weight, self.dh, self.dw, 0, workspace=self.ws_b)
 
 
-def cpu_baseline(x, k, sample_tokens, row="main", shard_rows=None):
-    """The oracle, as it stands, on a bounded sample: the first pair of the
-    workload with each row cut to its first `sample_tokens` completion positions."""
+def cpu_baseline(x, k, sample_tokens, row="main", shard_rows=None, sample_pairs=1):
+    """The oracle, as it stands, on a bounded sample: the first `sample_pairs`
+    pairs of the workload, each row cut to its first `sample_tokens` completion
+    positions (0 = all of them)."""
     from oracle import dpo_oracle as O
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    rows = [0, 1]
+    rows = list(range(2 * sample_pairs))
     mask = x.mask[rows].copy()
-    for r in range(2):
-        on = np.flatnonzero(mask[r])
-        mask[r, on[sample_tokens:]] = 0
+    if sample_tokens > 0:
+        for r in range(len(rows)):
+            on = np.flatnonzero(mask[r])
+            mask[r, on[sample_tokens:]] = 0
     tg = np.where(mask != 0, x.targets[rows], -100)
     n = int(mask.astype(np.int64).sum())
     t0 = time.perf_counter()
     if x.logits is not None and x.logits.dtype == np.float32:
         fwd = O.logits_f32_seq_logps(x.logits[rows], tg, mask)
         loss = O.dpo_loss(fwd["logp_sum"], fwd["logp_sum"] + x.ref_noise[rows], x.beta, x.layout)
-        O.logits_f32_backward_rows(x.logits[rows], tg, mask, fwd["lse"], loss["weight"], np.arange(2 * x.T))
+        for c in range(0, len(rows) * x.T, 256):  # dlogits of 256 positions at a time
+            O.logits_f32_backward_rows(x.logits[rows], tg, mask, fwd["lse"], loss["weight"], np.arange(c, c + 256))
         what = "fp32 logits fwd+loss+bwd"
     elif x.logits is not None:
         fwd = O.logits_seq_logps(x.logits[rows], tg, mask)
         loss = O.dpo_loss(fwd["logp_sum"], fwd["logp_sum"] + x.ref_noise[rows], x.beta, x.layout)
-        O.logits_backward_rows(x.logits[rows], tg, mask, fwd["lse"], loss["weight"],
-                               np.arange(2 * x.T))
+        for c in range(0, len(rows) * x.T, 256):  # dlogits of 256 positions at a time
+            O.logits_backward_rows(x.logits[rows], tg, mask, fwd["lse"], loss["weight"], np.arange(c, c + 256))
         what = "fwd+loss+bwd"
     elif row == "vocab-shard":
         hid = O.bf16_to_f64(x.hidden[rows])
@@ -325,8 +332,9 @@ def cpu_baseline(x, k, sample_tokens, row="main", shard_rows=None):
                                    "loss-variant": " with the length-normalised loss and NLL term"}.get(row, ""))
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "completion tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first pair, {sample_tokens} completion positions per row ({n} tokens), "
-                      f"{what}, {dt:.1f} s"}
+            "sample": f"first {'pair' if sample_pairs == 1 else f'{sample_pairs} pairs'}, "
+                      f"{f'{sample_tokens} completion positions per row' if sample_tokens > 0 else 'every completion position'} "
+                      f"({n} tokens), {what}, {dt:.1f} s"}
 
 
 def main():
@@ -441,8 +449,10 @@ def main():
     cpu = None
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(x, a.workload, a.cpu_sample_tokens, row,
-                           runner.Vs if row == "vocab-shard" else None)
+        given_logits = x.logits is not None
+        tokens = a.cpu_sample_tokens if a.cpu_sample_tokens is not None else (0 if given_logits else 1024)
+        pairs = a.cpu_sample_pairs if a.cpu_sample_pairs is not None else (x.num_pairs if given_logits else 1)
+        cpu = cpu_baseline(x, a.workload, tokens, row, runner.Vs if row == "vocab-shard" else None, pairs)
 
     metric = METRICS[a.workload] if row == "main" else ROW_METRICS[row].format(
         H=H, V=V, Vs=getattr(runner, "Vs", V))
