@@ -396,18 +396,34 @@ __global__ __launch_bounds__(256) void k_transpose_w(TransposeWArgs a) {
 }
 
 // hidden rows at completion positions -> HT [H, Mp], zero columns m >= n_c.
+// 64 positions x 64 hidden columns per block, 16-byte loads and stores.
 __global__ __launch_bounds__(256) void k_gather_ht(GatherHTArgs a) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ uint16_t tile[64][72];
   const int n_c = a.hdr->n_c;
   const int m0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
   if (m0 >= (int)align_up((size_t)n_c, BM)) return;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = it * 256 + tid;  // 64 positions x 8 chunks of 8 hidden columns
+    const int r = q >> 3, c = q & 7;
     const int m = m0 + r;
-    tile[r][tx] = m < n_c ? a.hidden[(size_t)a.idx[m] * a.H + h0 + tx] : (uint16_t)0;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (m < n_c) val = *(const u32x4*)(a.hidden + (size_t)a.idx[m] * a.H + h0 + c * 8);
+    *(u32x4*)&tile[r][c * 8] = val;
   }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) a.ht[(size_t)(h0 + r) * a.ldt + m0 + tx] = tile[tx][r];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = it * 256 + tid;  // 64 hidden rows x 8 chunks of 8 positions
+    const int h = q >> 3, c = q & 7;
+    uint32_t w4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w4[u] = (uint32_t)tile[c * 8 + 2 * u][h] | ((uint32_t)tile[c * 8 + 2 * u + 1][h] << 16);
+    const u32x4 o = {w4[0], w4[1], w4[2], w4[3]};
+    *(u32x4*)(a.ht + (size_t)(h0 + h) * a.ldt + m0 + c * 8) = o;
+  }
 }
 
 // ---------------------------------------------------------------------------
