@@ -34,6 +34,8 @@ constexpr int kSlotSlices = 4;
 // bytes (balanced slices of whole 256-wide tiles).
 constexpr size_t kChunkBytes = size_t(1) << 30;
 constexpr int kTransPad = 64;  // elements
+// workgroups per CU of the chunked streaming backward
+constexpr int kStreamBwdBlocksPerCU = 32;
 
 // ---------------------------------------------------------------------------
 // workspace layout
@@ -787,9 +789,9 @@ int logits_backward(const void* logits, bool f32, const int32_t* targets, const 
   b.hdr = hdr;
   b.d_logits = d_logits;
   if (f32)
-    RUN("stream_bwd_f32", launch_stream_bwd_f32(b, (long)rows * T, st));
+    RUN("stream_bwd_f32", launch_stream_bwd_f32(b, (long)rows * T, persistent_grid() * kStreamBwdBlocksPerCU, st));
   else
-    RUN("stream_bwd", launch_stream_bwd(b, (long)rows * T, st));
+    RUN("stream_bwd", launch_stream_bwd(b, (long)rows * T, persistent_grid() * kStreamBwdBlocksPerCU, st));
   return DPO_OK;
 }
 }  // namespace

@@ -8,8 +8,8 @@
 //   k_stream_fwd   one workgroup per completion position: a single pass over
 //                  the V logits with a running (max, sum exp) per lane, 16-byte
 //                  loads, then a fixed-order cross-lane combine -> lse, log p
-//   k_stream_bwd   one workgroup per position: dlogits = w (exp(x - lse) - onehot)
-//                  rounded to bf16, exactly zero at positions outside the mask
+//   k_stream_bwd   dlogits = w (exp(x - lse) - onehot) rounded to bf16, exactly
+//                  zero at positions outside the mask, in 16 KiB chunks
 //   k_loss         the sigmoid DPO loss, its per-row gradient weights, rewards,
 //                  margins and accuracy, in fp64 ("A worked example of the numbers"),
 //                  with the reference-free, length-normalised and NLL-term variants
@@ -133,39 +133,52 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_fwd(StreamFwdArgs a) 
   }
 }
 
-constexpr int kBwdUnroll = 8;
+// The backward walks [positions x V] in 16 KiB chunks (four 16-byte vectors
+// per thread), consecutive workgroups on consecutive chunks: the chunks in
+// flight at any moment form one contiguous stretch of the logits and of
+// dlogits, which this part reads and writes back ~8 % faster than one
+// workgroup per 256 KiB row (the rows' streams then sit 256 KiB apart).
+constexpr int kBwdVecs = 4;
+constexpr int kBwdChunk = kBwdVecs * kStreamThreads;  // 16-byte vectors per chunk
 
 template <typename E>
-__global__ __launch_bounds__(kStreamThreads) void k_stream_bwd(StreamBwdArgs a) {
+__global__ __launch_bounds__(kStreamThreads) void k_stream_bwd(StreamBwdArgs a, long positions) {
   constexpr int N = Elem<E>::kPerVec;
-  const size_t p = blockIdx.x;
   const int tid = threadIdx.x;
   const int nvec = a.V / N;
-  u32x4* out = (u32x4*)((E*)a.d_logits + p * a.V);
-  if (a.mask[p] == 0) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int v = tid; v < nvec; v += kStreamThreads) __builtin_nontemporal_store(z, out + v);
-    return;
-  }
-  int tg = a.targets[p];
-  if (tg < 0 || tg >= a.V) {
-    if (tid == 0) atomicOr(&a.hdr->status, kStatusTargetRange);
-    tg = -1;
-  }
-  const float L = a.lse[p] * kLog2e;
-  const float w = a.weight[p / a.T];
-  const int tv = tg >= 0 ? tg / N : -1;  // the one vector holding the target
-  const u32x4* row = (const u32x4*)((const E*)a.logits + p * a.V);
-  for (int v0 = tid; v0 < nvec; v0 += kBwdUnroll * kStreamThreads) {
-    u32x4 buf[kBwdUnroll];
+  const int cpr = (nvec + kBwdChunk - 1) / kBwdChunk;  // chunks per row
+  const long total = positions * cpr;
+  for (long c = blockIdx.x; c < total; c += gridDim.x) {
+    const long p = c / cpr;
+    const int v0 = (int)(c - p * cpr) * kBwdChunk;
+    u32x4* out = (u32x4*)((E*)a.d_logits + p * a.V);
+    if (a.mask[p] == 0) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < kBwdUnroll; ++u) {
-      const int v = v0 + u * kStreamThreads;
+      for (int u = 0; u < kBwdVecs; ++u) {
+        const int v = v0 + u * kStreamThreads + tid;
+        if (v < nvec) __builtin_nontemporal_store(z, out + v);
+      }
+      continue;
+    }
+    int tg = a.targets[p];
+    if (tg < 0 || tg >= a.V) {
+      if (tid == 0 && v0 == 0) atomicOr(&a.hdr->status, kStatusTargetRange);
+      tg = -1;
+    }
+    const float L = a.lse[p] * kLog2e;
+    const float w = a.weight[p / a.T];
+    const int tv = tg >= 0 ? tg / N : -1;  // the one vector holding the target
+    const u32x4* row = (const u32x4*)((const E*)a.logits + p * a.V);
+    u32x4 buf[kBwdVecs];
+#pragma unroll
+    for (int u = 0; u < kBwdVecs; ++u) {
+      const int v = v0 + u * kStreamThreads + tid;
       if (v < nvec) buf[u] = __builtin_nontemporal_load(row + v);
     }
 #pragma unroll
-    for (int u = 0; u < kBwdUnroll; ++u) {
-      const int v = v0 + u * kStreamThreads;
+    for (int u = 0; u < kBwdVecs; ++u) {
+      const int v = v0 + u * kStreamThreads + tid;
       if (v >= nvec) break;
       float x[N], d[N];
       Elem<E>::unpack(buf[u], x);
@@ -313,8 +326,15 @@ hipError_t launch_stream_fwd(const StreamFwdArgs& a, long positions, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, hipStream_t s) {
-  hipLaunchKernelGGL(k_stream_bwd<uint16_t>, dim3((unsigned)positions), dim3(kStreamThreads), 0, s, a);
+// grid: workgroups in flight (a multiple of the CU count); they stride over the chunks
+static unsigned bwd_grid(const StreamBwdArgs& a, long positions, int elems_per_vec, int grid) {
+  const long cpr = (a.V / elems_per_vec + kBwdChunk - 1) / kBwdChunk;
+  return (unsigned)std::max(1L, std::min<long>(positions * cpr, grid));
+}
+
+hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_stream_bwd<uint16_t>, dim3(bwd_grid(a, positions, 8, grid)), dim3(kStreamThreads), 0, s, a,
+                     positions);
   return hipGetLastError();
 }
 
@@ -323,8 +343,9 @@ hipError_t launch_stream_fwd_f32(const StreamFwdArgs& a, long positions, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_stream_bwd_f32(const StreamBwdArgs& a, long positions, hipStream_t s) {
-  hipLaunchKernelGGL(k_stream_bwd<float>, dim3((unsigned)positions), dim3(kStreamThreads), 0, s, a);
+hipError_t launch_stream_bwd_f32(const StreamBwdArgs& a, long positions, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_stream_bwd<float>, dim3(bwd_grid(a, positions, 4, grid)), dim3(kStreamThreads), 0, s, a,
+                     positions);
   return hipGetLastError();
 }
 

@@ -241,13 +241,13 @@ hipError_t launch_sort_targets(const SortArgs& a, hipStream_t s);
 hipError_t launch_onehot_dw(const OnehotDwArgs& a, int Mp, hipStream_t s);
 constexpr int kSortThreads = 1024;
 hipError_t launch_stream_fwd(const StreamFwdArgs& a, long positions, hipStream_t s);
-hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, hipStream_t s);
+hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, int grid, hipStream_t s);
 hipError_t launch_reset_status(WsHeader* hdr, hipStream_t s);
 hipError_t launch_loss(const LossArgs& a, hipStream_t s);
 hipError_t launch_shard_partials(const ShardPartialArgs& a, int Mp, hipStream_t s);
 hipError_t launch_shard_combine(const ShardCombineArgs& a, int Mp, hipStream_t s);
 hipError_t launch_stream_fwd_f32(const StreamFwdArgs& a, long positions, hipStream_t s);
-hipError_t launch_stream_bwd_f32(const StreamBwdArgs& a, long positions, hipStream_t s);
+hipError_t launch_stream_bwd_f32(const StreamBwdArgs& a, long positions, int grid, hipStream_t s);
 
 struct LogitsMeanArgs {
   const double* logit_sum;  // [2B]
