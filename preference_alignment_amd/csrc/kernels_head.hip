@@ -45,54 +45,66 @@ using namespace gemm;
 // completion positions
 // ---------------------------------------------------------------------------
 constexpr int kCompactThreads = 1024;
+constexpr int kCompactWaves = kCompactThreads / 64;
 
+// One workgroup walks the positions in rounds of 1,024 consecutive ones
+// (thread t takes position 1024 r + t, so loads and stores are coalesced).
+// A position's output slot is the running count of earlier rounds plus the
+// count of earlier waves in its round (a 16-entry LDS table, double buffered
+// so each round needs one barrier) plus its rank among the wave's set mask
+// lanes (a ballot).  Row-major ascending order falls out of this directly.
 __global__ __launch_bounds__(kCompactThreads) void k_compact(CompactArgs a) {
-  __shared__ int scan[kCompactThreads];
+  __shared__ int wtot[2][kCompactWaves];
   __shared__ int err;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const long N = (long)a.rows * a.T;
-  const long per = (N + kCompactThreads - 1) / kCompactThreads;
-  const long lo = min(N, per * tid);
-  const long hi = min(N, lo + per);
   if (tid == 0) err = 0;
-  int cnt = 0;
-  for (long p = lo; p < hi; ++p) cnt += a.mask[p] != 0;
-  scan[tid] = cnt;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over the thread counts
-  for (int o = 1; o < kCompactThreads; o <<= 1) {
-    int v = tid >= o ? scan[tid - o] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  int pos = scan[tid] - cnt;
-  const int n_c = scan[kCompactThreads - 1];
+  const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  int base = 0;  // completion positions before this round
   int bad = 0;
-  for (long p = lo; p < hi; ++p) {
-    if (p % a.T == 0) a.row_off[p / a.T] = pos;
-    if (a.mask[p] != 0) {
-      int t = a.targets[p];
-      if (t < 0 || t >= a.V_total) {
-        bad = 1;
-        t = -1;
+  for (long r0 = 0, round = 0; r0 < N; r0 += kCompactThreads, ++round) {
+    const long p = r0 + tid;
+    const bool in = p < N;
+    const bool on = in && a.mask[p] != 0;
+    const unsigned long long bal = __ballot(on);
+    const int buf = (int)(round & 1);
+    if (lane == 0) wtot[buf][wave] = __popcll(bal);
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kCompactWaves; ++w) {
+      const int c = wtot[buf][w];
+      before += w < wave ? c : 0;
+      total += c;
+    }
+    const int pos = base + before + __popcll(bal & lt_mask);
+    if (in) {
+      if (p % a.T == 0) a.row_off[p / a.T] = pos;
+      if (on) {
+        int t = a.targets[p];
+        if (t < 0 || t >= a.V_total) {
+          bad = 1;
+          t = -1;
+        } else {
+          t -= a.v_begin;
+          if (t < 0 || t >= a.V) t = -1;  // held by another vocabulary shard
+        }
+        a.idx[pos] = (int)p;
+        a.tgt_c[pos] = t;
+        a.row_c[pos] = (int)(p / a.T);
       } else {
-        t -= a.v_begin;
-        if (t < 0 || t >= a.V) t = -1;  // held by another vocabulary shard
-      }
-      a.idx[pos] = (int)p;
-      a.tgt_c[pos] = t;
-      a.row_c[pos] = (int)(p / a.T);
-      ++pos;
-    } else {
-      if (a.lse_out) a.lse_out[p] = 0.f;
-      if (a.off_max) {
-        a.off_max[p] = -INFINITY;
-        a.off_sum[p] = 0.f;
-        a.off_tgt[p] = -INFINITY;
+        if (a.lse_out) a.lse_out[p] = 0.f;
+        if (a.off_max) {
+          a.off_max[p] = -INFINITY;
+          a.off_sum[p] = 0.f;
+          a.off_tgt[p] = -INFINITY;
+        }
       }
     }
+    base += total;
   }
+  const int n_c = base;
   if (bad) atomicOr(&err, kStatusTargetRange);
   // padding entries up to the padded position count: a valid row, no target
   for (long m = n_c + tid; m < a.Mp; m += kCompactThreads) {
