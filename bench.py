@@ -112,7 +112,7 @@ def parse():
                    help="completion positions per sampled row for the CPU baseline (0 = all); "
                         "default 1024 for the fused head, all for given logits")
     p.add_argument("--cpu-sample-pairs", type=int, default=None,
-                   help="pairs in the CPU baseline sample; default 1 for the fused head, all for given logits")
+                   help="pairs in the CPU baseline sample; default 1 for the fused head, 2 for given logits")
     p.add_argument("--no-kernel-timing", action="store_true")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
     p.add_argument("--row", default="main", choices=ROWS,
@@ -451,7 +451,7 @@ def main():
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         given_logits = x.logits is not None
         tokens = a.cpu_sample_tokens if a.cpu_sample_tokens is not None else (0 if given_logits else 1024)
-        pairs = a.cpu_sample_pairs if a.cpu_sample_pairs is not None else (x.num_pairs if given_logits else 1)
+        pairs = a.cpu_sample_pairs if a.cpu_sample_pairs is not None else (min(2, x.num_pairs) if given_logits else 1)
         cpu = cpu_baseline(x, a.workload, tokens, row, runner.Vs if row == "vocab-shard" else None, pairs)
 
     metric = METRICS[a.workload] if row == "main" else ROW_METRICS[row].format(
