@@ -123,6 +123,21 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+class _Dev:
+    """Pointers of the call's tensors, all on one GPU; the call runs with that
+    GPU current (the library launches on the current device)."""
+
+    def __init__(self, anchor):
+        self.dev = anchor.device
+
+    def p(self, t) -> Optional[int]:
+        if t is None:
+            return None
+        if t.device != self.dev:
+            raise ValueError(f"tensors on {t.device} and {self.dev}: all arguments must be on one GPU")
+        return t.data_ptr()
+
+
 def _stream(stream, like=None):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
@@ -176,9 +191,11 @@ def dpo_seq_logps(hidden, w_vocab, targets, mask, logp_sum, logp_sum64=None, lse
     if n_tokens is not None:
         _need(n_tokens, torch.int32, "n_tokens", (rows,))
     _need(workspace, torch.uint8, "workspace")
-    _check(lib().dpo_seq_logps(_ptr(hidden), _ptr(w_vocab), _ptr(targets), _ptr(mask), rows, T, H, V,
-                               _ptr(logp_sum), _ptr(logp_sum64), _ptr(lse), _ptr(n_tokens),
-                               _ptr(workspace), workspace.numel(), _stream(stream, hidden)))
+    _d = _Dev(hidden)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_seq_logps(_d.p(hidden), _d.p(w_vocab), _d.p(targets), _d.p(mask), rows, T, H, V,
+                                   _d.p(logp_sum), _d.p(logp_sum64), _d.p(lse), _d.p(n_tokens),
+                                   _d.p(workspace), workspace.numel(), _stream(stream, hidden)))
 
 
 def dpo_ref_score(hidden, w_vocab, targets, mask, ref_sum, workspace=None, stream=None) -> None:
@@ -191,8 +208,10 @@ def dpo_ref_score(hidden, w_vocab, targets, mask, ref_sum, workspace=None, strea
     _need(mask, torch.uint8, "mask", (rows, T))
     _need(ref_sum, torch.float32, "ref_sum", (rows,))
     _need(workspace, torch.uint8, "workspace")
-    _check(lib().dpo_ref_score(_ptr(hidden), _ptr(w_vocab), _ptr(targets), _ptr(mask), rows, T, H, V,
-                               _ptr(ref_sum), _ptr(workspace), workspace.numel(), _stream(stream, hidden)))
+    _d = _Dev(hidden)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_ref_score(_d.p(hidden), _d.p(w_vocab), _d.p(targets), _d.p(mask), rows, T, H, V,
+                                   _d.p(ref_sum), _d.p(workspace), workspace.numel(), _stream(stream, hidden)))
 
 
 def dpo_loss(policy_sum64, ref_sum, beta: float, layout: int, loss, weight, reward=None, margin=None,
@@ -211,9 +230,11 @@ def dpo_loss(policy_sum64, ref_sum, beta: float, layout: int, loss, weight, rewa
         _need(accuracy, torch.float32, "accuracy", (1,))
     if R % 2:
         raise ValueError("rows must be even")
-    _check(lib().dpo_loss(_ptr(policy_sum64), _ptr(ref_sum), R // 2, float(beta), int(layout), _ptr(loss),
-                          _ptr(weight), _ptr(reward), _ptr(margin), _ptr(accuracy),
-                          _stream(stream, policy_sum64)))
+    _d = _Dev(policy_sum64)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_loss(_d.p(policy_sum64), _d.p(ref_sum), R // 2, float(beta), int(layout), _d.p(loss),
+                              _d.p(weight), _d.p(reward), _d.p(margin), _d.p(accuracy),
+                              _stream(stream, policy_sum64)))
 
 
 def dpo_head_backward(hidden, w_vocab, targets, mask, lse, weight, d_hidden, d_w_vocab,
@@ -230,9 +251,11 @@ def dpo_head_backward(hidden, w_vocab, targets, mask, lse, weight, d_hidden, d_w
     _need(d_hidden, torch.float32, "d_hidden", (rows, T, H))
     _need(d_w_vocab, torch.float32, "d_w_vocab", (V, H))
     _need(workspace, torch.uint8, "workspace")
-    _check(lib().dpo_head_backward(_ptr(hidden), _ptr(w_vocab), _ptr(targets), _ptr(mask), rows, T, H, V,
-                                   _ptr(lse), _ptr(weight), _ptr(d_hidden), _ptr(d_w_vocab), int(accumulate_dw),
-                                   _ptr(workspace), workspace.numel(), _stream(stream, hidden)))
+    _d = _Dev(hidden)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_head_backward(_d.p(hidden), _d.p(w_vocab), _d.p(targets), _d.p(mask), rows, T, H, V,
+                                       _d.p(lse), _d.p(weight), _d.p(d_hidden), _d.p(d_w_vocab), int(accumulate_dw),
+                                       _d.p(workspace), workspace.numel(), _stream(stream, hidden)))
 
 
 def dpo_logits_seq_logps(logits, targets, mask, logp_sum, logp_sum64=None, lse=None, n_tokens=None,
@@ -250,9 +273,11 @@ def dpo_logits_seq_logps(logits, targets, mask, logp_sum, logp_sum64=None, lse=N
     if n_tokens is not None:
         _need(n_tokens, torch.int32, "n_tokens", (rows,))
     _need(workspace, torch.uint8, "workspace")
-    _check(lib().dpo_logits_seq_logps(_ptr(logits), _ptr(targets), _ptr(mask), rows, T, V, _ptr(logp_sum),
-                                      _ptr(logp_sum64), _ptr(lse), _ptr(n_tokens), _ptr(workspace),
-                                      workspace.numel(), _stream(stream, logits)))
+    _d = _Dev(logits)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_logits_seq_logps(_d.p(logits), _d.p(targets), _d.p(mask), rows, T, V, _d.p(logp_sum),
+                                          _d.p(logp_sum64), _d.p(lse), _d.p(n_tokens), _d.p(workspace),
+                                          workspace.numel(), _stream(stream, logits)))
 
 
 def dpo_logits_backward(logits, targets, mask, lse, weight, d_logits, workspace=None, stream=None) -> None:
@@ -265,9 +290,11 @@ def dpo_logits_backward(logits, targets, mask, lse, weight, d_logits, workspace=
     _need(weight, torch.float32, "weight", (rows,))
     _need(d_logits, torch.bfloat16, "d_logits", (rows, T, V))
     _need(workspace, torch.uint8, "workspace")
-    _check(lib().dpo_logits_backward(_ptr(logits), _ptr(targets), _ptr(mask), rows, T, V, _ptr(lse),
-                                     _ptr(weight), _ptr(d_logits), _ptr(workspace), workspace.numel(),
-                                     _stream(stream, logits)))
+    _d = _Dev(logits)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_logits_backward(_d.p(logits), _d.p(targets), _d.p(mask), rows, T, V, _d.p(lse),
+                                         _d.p(weight), _d.p(d_logits), _d.p(workspace), workspace.numel(),
+                                         _stream(stream, logits)))
 
 
 def dpo_loss_ex(policy_sum64, ref_sum, n_tokens, beta: float, layout: int, flags: int, sft_alpha: float,
@@ -287,10 +314,12 @@ def dpo_loss_ex(policy_sum64, ref_sum, n_tokens, beta: float, layout: int, flags
             _need(t, torch.float32, name, shape)
     if R % 2:
         raise ValueError("rows must be even")
-    _check(lib().dpo_loss_ex(_ptr(policy_sum64), _ptr(ref_sum), _ptr(n_tokens), R // 2, float(beta),
-                             int(layout), int(flags), float(sft_alpha), _ptr(loss), _ptr(weight),
-                             _ptr(reward), _ptr(margin), _ptr(accuracy), _ptr(nll),
-                             _stream(stream, policy_sum64)))
+    _d = _Dev(policy_sum64)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_loss_ex(_d.p(policy_sum64), _d.p(ref_sum), _d.p(n_tokens), R // 2, float(beta),
+                                 int(layout), int(flags), float(sft_alpha), _d.p(loss), _d.p(weight),
+                                 _d.p(reward), _d.p(margin), _d.p(accuracy), _d.p(nll),
+                                 _stream(stream, policy_sum64)))
 
 
 def dpo_logits_f32_seq_logps(logits, targets, mask, logp_sum, logp_sum64=None, lse=None, n_tokens=None,
@@ -308,9 +337,11 @@ def dpo_logits_f32_seq_logps(logits, targets, mask, logp_sum, logp_sum64=None, l
     if n_tokens is not None:
         _need(n_tokens, torch.int32, "n_tokens", (rows,))
     _need(workspace, torch.uint8, "workspace")
-    _check(lib().dpo_logits_f32_seq_logps(_ptr(logits), _ptr(targets), _ptr(mask), rows, T, V,
-                                          _ptr(logp_sum), _ptr(logp_sum64), _ptr(lse), _ptr(n_tokens),
-                                          _ptr(workspace), workspace.numel(), _stream(stream, logits)))
+    _d = _Dev(logits)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_logits_f32_seq_logps(_d.p(logits), _d.p(targets), _d.p(mask), rows, T, V,
+                                              _d.p(logp_sum), _d.p(logp_sum64), _d.p(lse), _d.p(n_tokens),
+                                              _d.p(workspace), workspace.numel(), _stream(stream, logits)))
 
 
 def dpo_logits_f32_backward(logits, targets, mask, lse, weight, d_logits, workspace=None,
@@ -324,9 +355,11 @@ def dpo_logits_f32_backward(logits, targets, mask, lse, weight, d_logits, worksp
     _need(weight, torch.float32, "weight", (rows,))
     _need(d_logits, torch.float32, "d_logits", (rows, T, V))
     _need(workspace, torch.uint8, "workspace")
-    _check(lib().dpo_logits_f32_backward(_ptr(logits), _ptr(targets), _ptr(mask), rows, T, V, _ptr(lse),
-                                         _ptr(weight), _ptr(d_logits), _ptr(workspace), workspace.numel(),
-                                         _stream(stream, logits)))
+    _d = _Dev(logits)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_logits_f32_backward(_d.p(logits), _d.p(targets), _d.p(mask), rows, T, V, _d.p(lse),
+                                             _d.p(weight), _d.p(d_logits), _d.p(workspace), workspace.numel(),
+                                             _stream(stream, logits)))
 
 
 def dpo_seq_logps_shard(hidden, w_shard, targets, mask, v_begin: int, V_total: int, part_max, part_sumexp,
@@ -341,10 +374,12 @@ def dpo_seq_logps_shard(hidden, w_shard, targets, mask, v_begin: int, V_total: i
     for t, name in ((part_max, "part_max"), (part_sumexp, "part_sumexp"), (part_tgt, "part_tgt")):
         _need(t, torch.float32, name, (rows, T))
     _need(workspace, torch.uint8, "workspace")
-    _check(lib().dpo_seq_logps_shard(_ptr(hidden), _ptr(w_shard), _ptr(targets), _ptr(mask), rows, T, H, Vs,
-                                     int(v_begin), int(V_total), _ptr(part_max), _ptr(part_sumexp),
-                                     _ptr(part_tgt), _ptr(workspace), workspace.numel(),
-                                     _stream(stream, hidden)))
+    _d = _Dev(hidden)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_seq_logps_shard(_d.p(hidden), _d.p(w_shard), _d.p(targets), _d.p(mask), rows, T, H, Vs,
+                                         int(v_begin), int(V_total), _d.p(part_max), _d.p(part_sumexp),
+                                         _d.p(part_tgt), _d.p(workspace), workspace.numel(),
+                                         _stream(stream, hidden)))
 
 
 def dpo_shard_combine(part_max, part_sumexp, part_tgt, targets, mask, V_total: int, logp_sum, logp_sum64=None,
@@ -363,10 +398,12 @@ def dpo_shard_combine(part_max, part_sumexp, part_tgt, targets, mask, V_total: i
     if n_tokens is not None:
         _need(n_tokens, torch.int32, "n_tokens", (rows,))
     _need(workspace, torch.uint8, "workspace")
-    _check(lib().dpo_shard_combine(_ptr(part_max), _ptr(part_sumexp), _ptr(part_tgt), S, _ptr(targets),
-                                   _ptr(mask), rows, T, int(V_total), _ptr(logp_sum), _ptr(logp_sum64),
-                                   _ptr(lse), _ptr(n_tokens), _ptr(workspace), workspace.numel(),
-                                   _stream(stream, part_max)))
+    _d = _Dev(part_max)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_shard_combine(_d.p(part_max), _d.p(part_sumexp), _d.p(part_tgt), S, _d.p(targets),
+                                       _d.p(mask), rows, T, int(V_total), _d.p(logp_sum), _d.p(logp_sum64),
+                                       _d.p(lse), _d.p(n_tokens), _d.p(workspace), workspace.numel(),
+                                       _stream(stream, part_max)))
 
 
 def dpo_head_backward_shard(hidden, w_shard, targets, mask, v_begin: int, V_total: int, lse, weight,
@@ -383,10 +420,12 @@ def dpo_head_backward_shard(hidden, w_shard, targets, mask, v_begin: int, V_tota
     _need(d_hidden, torch.float32, "d_hidden", (rows, T, H))
     _need(d_w_shard, torch.float32, "d_w_shard", (Vs, H))
     _need(workspace, torch.uint8, "workspace")
-    _check(lib().dpo_head_backward_shard(_ptr(hidden), _ptr(w_shard), _ptr(targets), _ptr(mask), rows, T, H,
-                                         Vs, int(v_begin), int(V_total), _ptr(lse), _ptr(weight),
-                                         _ptr(d_hidden), _ptr(d_w_shard), int(accumulate_dw),
-                                         _ptr(workspace), workspace.numel(), _stream(stream, hidden)))
+    _d = _Dev(hidden)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_head_backward_shard(_d.p(hidden), _d.p(w_shard), _d.p(targets), _d.p(mask), rows, T, H,
+                                             Vs, int(v_begin), int(V_total), _d.p(lse), _d.p(weight),
+                                             _d.p(d_hidden), _d.p(d_w_shard), int(accumulate_dw),
+                                             _d.p(workspace), workspace.numel(), _stream(stream, hidden)))
 
 
 def dpo_seq_logps_metrics(hidden, w_vocab, targets, mask, logp_sum, logit_sum, logp_sum64=None, lse=None,
@@ -407,10 +446,12 @@ def dpo_seq_logps_metrics(hidden, w_vocab, targets, mask, logp_sum, logit_sum, l
     if n_tokens is not None:
         _need(n_tokens, torch.int32, "n_tokens", (rows,))
     _need(workspace, torch.uint8, "workspace")
-    _check(lib().dpo_seq_logps_metrics(_ptr(hidden), _ptr(w_vocab), _ptr(targets), _ptr(mask), rows, T, H, V,
-                                       _ptr(logp_sum), _ptr(logp_sum64), _ptr(lse), _ptr(n_tokens),
-                                       _ptr(logit_sum), _ptr(workspace), workspace.numel(),
-                                       _stream(stream, hidden)))
+    _d = _Dev(hidden)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_seq_logps_metrics(_d.p(hidden), _d.p(w_vocab), _d.p(targets), _d.p(mask), rows, T, H, V,
+                                           _d.p(logp_sum), _d.p(logp_sum64), _d.p(lse), _d.p(n_tokens),
+                                           _d.p(logit_sum), _d.p(workspace), workspace.numel(),
+                                           _stream(stream, hidden)))
 
 
 def dpo_logits_mean(logit_sum, n_tokens, V: int, layout: int, means, stream=None) -> None:
@@ -421,13 +462,17 @@ def dpo_logits_mean(logit_sum, n_tokens, V: int, layout: int, means, stream=None
     _need(means, torch.float32, "means", (2,))
     if R % 2:
         raise ValueError("rows must be even")
-    _check(lib().dpo_logits_mean(_ptr(logit_sum), _ptr(n_tokens), R // 2, int(V), int(layout), _ptr(means),
-                                 _stream(stream, logit_sum)))
+    _d = _Dev(logit_sum)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_logits_mean(_d.p(logit_sum), _d.p(n_tokens), R // 2, int(V), int(layout), _d.p(means),
+                                     _stream(stream, logit_sum)))
 
 
 def dpo_device_status(workspace, stream=None) -> int:
     """Waits for the stream; raises DpoError on a device-detected error."""
-    st = lib().dpo_device_status(_ptr(workspace), _stream(stream, workspace))
+    import torch
+    with torch.cuda.device(workspace.device):
+        st = lib().dpo_device_status(_ptr(workspace), _stream(stream, workspace))
     _check(st)
     return st
 

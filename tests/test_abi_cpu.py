@@ -187,3 +187,18 @@ def test_shard_and_f32_and_metrics_validation(L):
     assert L.dpo_logits_mean(FAKE, FAKE, 2, 1024, 5, FAKE, None) == D.DPO_ERR_LAYOUT
     assert L.dpo_logits_mean(FAKE, None, 2, 1024, 0, FAKE, None) == D.DPO_ERR_NULL
     assert D.dpo_strerror(D.DPO_ERR_ALPHA).startswith("sft_alpha")
+
+
+def test_binding_keeps_every_argument_on_one_gpu():
+    class Fake:
+        def __init__(self, dev):
+            self.device = dev
+
+        def data_ptr(self):
+            return FAKE
+
+    d = D._Dev(Fake("cuda:0"))
+    assert d.p(Fake("cuda:0")) == FAKE
+    assert d.p(None) is None
+    with pytest.raises(ValueError):
+        d.p(Fake("cuda:1"))
