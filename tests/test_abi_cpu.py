@@ -202,3 +202,21 @@ def test_binding_keeps_every_argument_on_one_gpu():
     assert d.p(None) is None
     with pytest.raises(ValueError):
         d.p(Fake("cuda:1"))
+
+
+def test_header_compiles_as_c_and_links(L, tmp_path):
+    """include/dpo_head.h is plain C99; a C program links the library and
+    makes host-only calls through it."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = os.path.join(os.path.dirname(__file__), "c_abi_host.c")
+    exe = str(tmp_path / "c_abi_host")
+    libdir = os.path.dirname(B.LIB_PATH)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(D.HEADER), src, "-o", exe,
+                    "-L", libdir, "-ldpohead", "-Wl,-rpath," + libdir], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "c abi ok" in r.stdout
