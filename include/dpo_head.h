@@ -263,7 +263,7 @@ int dpo_head_backward_shard(const dpo_bf16* hidden, const dpo_bf16* w_shard,
  * (workspace DPO_OP_SEQ_LOGPS_METRICS).  dpo_logits_mean turns the sums into
  *   means[0] = mean logit of the chosen rows, means[1] = of the rejected rows,
  * each over (completion positions x V); 0 for a half without tokens.  The
- * pages average over the whole logits tensor; this build has logits only at
+ * pages average over the whole logits tensor; this library has logits only at
  * completion positions, so the means cover those. */
 int dpo_seq_logps_metrics(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int32_t* targets,
                           const uint8_t* mask, int rows, int T, int H, int V, float* logp_sum,
