@@ -739,30 +739,30 @@ int logits_forward(const void* logits, bool f32, const int32_t* targets, const u
   hipStream_t st = (hipStream_t)stream;
   const Layout L = make_layout(DPO_OP_LOGITS_SEQ_LOGPS, rows, T, 0, V);
   void* ws = workspace;
-  rc = enqueue_compact(L, ws, targets, mask, rows, T, V, lse, st);
-  if (rc) return rc;
   StreamFwdArgs f;
   f.logits = logits;
+  f.targets = targets;
+  f.mask = mask;
   f.V = V;
-  f.idx = at<int>(ws, L.idx);
-  f.tgt_c = at<int>(ws, L.tgt);
   f.hdr = at<WsHeader>(ws, L.hdr);
-  f.lse64 = at<double>(ws, L.lse64);
   f.logp64 = at<double>(ws, L.logp64);
+  f.bad = at<int>(ws, L.idx);
   f.lse_out = lse;
   if (f32)
     RUN("stream_fwd_f32", launch_stream_fwd_f32(f, (long)rows * T, st));
   else
     RUN("stream_fwd", launch_stream_fwd(f, (long)rows * T, st));
-  RowSumArgs r;
+  StreamRowSumArgs r;
   r.logp64 = f.logp64;
-  r.row_off = at<int>(ws, L.rowoff);
+  r.bad = f.bad;
+  r.mask = mask;
   r.hdr = f.hdr;
   r.rows = rows;
+  r.T = T;
   r.sum32 = logp_sum;
   r.sum64 = logp_sum64;
   r.n_tokens = n_tokens;
-  RUN("row_sums", launch_row_sums(r, st));
+  RUN("row_sums", launch_stream_row_sums(r, st));
   return DPO_OK;
 }
 

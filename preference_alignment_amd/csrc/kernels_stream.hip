@@ -5,9 +5,10 @@
 // a caller that already holds the [rows x T x V] logits the page's memory
 // section sizes at 0.49 GiB per 2,048-token sequence in bf16.
 //
-//   k_stream_fwd   one workgroup per completion position: a single pass over
-//                  the V logits with a running (max, sum exp) per lane, 16-byte
-//                  loads, then a fixed-order cross-lane combine -> lse, log p
+//   k_stream_fwd   one workgroup per position (mask-0 ones only write zeros): a
+//                  single pass over the V logits with a running (max, sum exp)
+//                  per lane, 16-byte loads, then a fixed-order cross-lane
+//                  combine -> lse, log p; k_stream_row_sums then sums each row
 //   k_stream_bwd   dlogits = w (exp(x - lse) - onehot) rounded to bf16, exactly
 //                  zero at positions outside the mask, in 16 KiB chunks
 //   k_loss         the sigmoid DPO loss, its per-row gradient weights, rewards,
@@ -94,13 +95,25 @@ __device__ __forceinline__ void absorb(float& m, float& s, const u32x4 v) {
   s += acc;
 }
 
+// One workgroup per position of [rows, T]: a mask-0 position only writes its
+// zeros; a completion position reads its V logits once.  Per-position
+// results stay at the position's flat index (no compaction pass: the row
+// sums read the mask themselves), and a target outside [0, V) is recorded
+// in a per-position flag that the row sums turn into the status word.
 template <typename E>
 __global__ __launch_bounds__(kStreamThreads) void k_stream_fwd(StreamFwdArgs a) {
   __shared__ float2 red[kStreamThreads / 64];
-  const int m = blockIdx.x;
-  if (m >= a.hdr->n_c) return;
+  const size_t pos = blockIdx.x;
   const int tid = threadIdx.x;
-  const size_t pos = (size_t)a.idx[m];
+  if (pos == 0 && tid == 0) a.hdr->status = 0;  // the row sums run after this kernel and set it
+  if (a.mask[pos] == 0) {
+    if (tid == 0) {
+      a.logp64[pos] = 0.0;
+      a.bad[pos] = 0;
+      if (a.lse_out) a.lse_out[pos] = 0.f;
+    }
+    return;
+  }
   const u32x4* row = (const u32x4*)((const E*)a.logits + pos * a.V);
   const int nvec = a.V / Elem<E>::kPerVec;
   float mx = -INFINITY, s = 0.f;
@@ -126,10 +139,50 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_fwd(StreamFwdArgs a) 
     float M = red[0].x, S = red[0].y;
     for (int w = 1; w < kStreamThreads / 64; ++w) lse_merge(M, S, red[w].x, red[w].y);
     const double lse = (double)M + log((double)S);
-    const int t = a.tgt_c[m];
-    a.lse64[m] = lse;
-    a.logp64[m] = t >= 0 ? (double)Elem<E>::scalar(a.logits, pos * a.V + t) - lse : __builtin_nan("");
+    const int t = a.targets[pos];
+    const bool ok = t >= 0 && t < a.V;
+    a.logp64[pos] = ok ? (double)Elem<E>::scalar(a.logits, pos * a.V + t) - lse : __builtin_nan("");
+    a.bad[pos] = ok ? 0 : 1;
     if (a.lse_out) a.lse_out[pos] = (float)lse;
+  }
+}
+
+// Row sums over the flat per-position log p of the streaming forward, in a
+// fixed order (each thread a strided share of the row, then a tree), with
+// the row's completion count; a row holding an out-of-range target sets the
+// status word (reset by the forward kernel, which ran before).
+__global__ __launch_bounds__(256) void k_stream_row_sums(StreamRowSumArgs a) {
+  __shared__ double red[256];
+  __shared__ int cnt[256];
+  __shared__ int flag[256];
+  const int r = blockIdx.x;
+  const size_t base = (size_t)r * a.T;
+  double s = 0.0;
+  int c = 0, f = 0;
+  for (int t = threadIdx.x; t < a.T; t += 256) {
+    const bool on = a.mask[base + t] != 0;
+    s += on ? a.logp64[base + t] : 0.0;
+    c += on;
+    f |= on ? a.bad[base + t] : 0;
+  }
+  red[threadIdx.x] = s;
+  cnt[threadIdx.x] = c;
+  flag[threadIdx.x] = f;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      red[threadIdx.x] += red[threadIdx.x + o];
+      cnt[threadIdx.x] += cnt[threadIdx.x + o];
+      flag[threadIdx.x] |= flag[threadIdx.x + o];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double v = red[0];
+    if (a.sum32) a.sum32[r] = (float)v;
+    if (a.sum64) a.sum64[r] = v;
+    if (a.n_tokens) a.n_tokens[r] = cnt[0];
+    if (flag[0]) atomicOr(&a.hdr->status, kStatusTargetRange);
   }
 }
 
@@ -346,6 +399,11 @@ hipError_t launch_stream_fwd_f32(const StreamFwdArgs& a, long positions, hipStre
 hipError_t launch_stream_bwd_f32(const StreamBwdArgs& a, long positions, int grid, hipStream_t s) {
   hipLaunchKernelGGL(k_stream_bwd<float>, dim3(bwd_grid(a, positions, 4, grid)), dim3(kStreamThreads), 0, s, a,
                      positions);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_row_sums(const StreamRowSumArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_stream_row_sums, dim3(a.rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -190,13 +190,24 @@ struct ZeroRowsArgs {
 // logits; `logits` / `d_logits` point to that element type.
 struct StreamFwdArgs {
   const void* logits;  // [rows*T, V]
+  const int32_t* targets;  // [rows*T]
+  const uint8_t* mask;     // [rows*T]
   int V;
-  const int* idx;
-  const int* tgt_c;
-  const WsHeader* hdr;
-  double* lse64;
-  double* logp64;
-  float* lse_out;  // nullable
+  WsHeader* hdr;     // status word, reset here and set by the row sums
+  double* logp64;    // [rows*T] log p at completion positions, 0 elsewhere
+  int* bad;          // [rows*T] 1 where the target is outside [0, V)
+  float* lse_out;    // nullable
+};
+
+struct StreamRowSumArgs {
+  const double* logp64;
+  const int* bad;
+  const uint8_t* mask;
+  WsHeader* hdr;
+  int rows, T;
+  float* sum32;       // nullable
+  double* sum64;      // nullable
+  int32_t* n_tokens;  // nullable
 };
 
 struct StreamBwdArgs {
@@ -241,6 +252,7 @@ hipError_t launch_sort_targets(const SortArgs& a, hipStream_t s);
 hipError_t launch_onehot_dw(const OnehotDwArgs& a, int Mp, hipStream_t s);
 constexpr int kSortThreads = 1024;
 hipError_t launch_stream_fwd(const StreamFwdArgs& a, long positions, hipStream_t s);
+hipError_t launch_stream_row_sums(const StreamRowSumArgs& a, hipStream_t s);
 hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, int grid, hipStream_t s);
 hipError_t launch_reset_status(WsHeader* hdr, hipStream_t s);
 hipError_t launch_loss(const LossArgs& a, hipStream_t s);
