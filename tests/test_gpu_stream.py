@@ -63,7 +63,24 @@ CASES = {
 def test_logits_path_matches_oracle(case):
     dev = need_gpu()
     print(f"[gpu] logits parity case={case}", flush=True)
-    x = W.make_logits_inputs(name=case, **CASES[case])
+    _logits_check(W.make_logits_inputs(name=case, **CASES[case]), dev)
+
+
+def test_logits_path_empty_row_and_mask_holes():
+    """A row with no completion position (score 0, no tokens, zero gradient)
+    and holes inside another row's completion span."""
+    dev = need_gpu()
+    print("[gpu] logits parity case=holes", flush=True)
+    x = W.make_logits_inputs(name="holes", **CASES["small_ragged"])
+    x.mask[1, :] = 0
+    x.mask[2, 15:18] = 0
+    x.mask[3, 39] = 0
+    x.targets = np.where(x.mask != 0, x.targets, W.IGNORE_INDEX).astype(np.int32)
+    g = _logits_check(x, dev)
+    assert int(np_(g["n_tokens"])[1]) == 0 and float(np_(g["logp_sum64"])[1]) == 0.0
+
+
+def _logits_check(x, dev):
     d = dev_inputs(x, dev)
     fwd = O.logits_seq_logps(x.logits, x.targets, x.mask)
     g = stream_forward(x, d, dev)
@@ -80,6 +97,7 @@ def test_logits_path_matches_oracle(case):
     dl = stream_backward(x, d, g["lse"], weight, dev)
     check_dlogits_rows(x, dl, fwd["lse"], ol["weight"], np.arange(x.rows * x.T))
     assert torch.count_nonzero(dl[torch.from_numpy(~m).to(dev)]).item() == 0
+    return g
 
 
 def test_logits_path_out_of_range_target_is_reported():
