@@ -156,3 +156,121 @@ def test_full_size_ref_score_workload3():
     got = np_(out)
     print(f"  max |d ref_sum| = {np.abs(got - pi).max():.3e}", flush=True)
     assert np.all(np.abs(got - pi) <= LOGP_RTOL * np.maximum(1.0, np.abs(pi)))
+
+
+def test_full_size_vocab_shards_workload2():
+    """The 8B head's vocabulary in four V/4 shards, as one GPU of a TP=4 group
+    would hold them: shard partials at sampled positions from the definition,
+    the combine of the four shards against the stored whole-vocabulary sums and
+    lse, and two shards' backward at sampled positions and vocabulary rows."""
+    dev = need_gpu()
+    print("[gpu] full-size vocabulary shards, workload 2", flush=True)
+    gold = _golden(2)
+    x = W.make_workload(2)
+    assert _digest(x) == str(gold["digest"])
+    d = dev_inputs(x, dev)
+    R, T, H, V = x.rows, x.T, x.H, x.V
+    m = x.mask != 0
+    S = 4
+    cuts = [s * V // S for s in range(S + 1)]
+    pmax = torch.empty(S, R, T, dtype=torch.float32, device=dev)
+    psum, ptgt = torch.empty_like(pmax), torch.empty_like(pmax)
+    for s in range(S):
+        a, b = cuts[s], cuts[s + 1]
+        ws = D.alloc_workspace(D.DPO_OP_SEQ_LOGPS, R, T, H, b - a, dev)
+        D.dpo_seq_logps_shard(d["hidden"], d["w"][a:b].contiguous(), d["targets"], d["mask"], a, V, pmax[s],
+                              psum[s], ptgt[s], workspace=ws)
+        D.dpo_device_status(ws)
+        del ws
+    rng = np.random.default_rng(2002)
+    idx = np.flatnonzero(m.reshape(-1))
+    pos = np.sort(rng.choice(idx, size=16, replace=False))
+    W64 = O.bf16_to_f64(x.w_vocab)
+    hs = O.bf16_to_f64(x.hidden.reshape(R * T, H)[pos])
+    tg = x.targets.reshape(-1)[pos]
+    for s in range(S):
+        a, b = cuts[s], cuts[s + 1]
+        Z = hs @ W64[a:b].T
+        mx = Z.max(axis=1)
+        gm = np_(pmax[s]).reshape(-1)[pos]
+        gs = np_(psum[s]).reshape(-1)[pos]
+        gt = np_(ptgt[s]).reshape(-1)[pos]
+        np.testing.assert_allclose(gm, mx, rtol=0, atol=1e-5)
+        np.testing.assert_allclose(np.log(gs) + gm, np.log(np.exp(Z - mx[:, None]).sum(axis=1)) + mx, rtol=0,
+                                   atol=LSE_ATOL)
+        mine = (tg >= a) & (tg < b)
+        assert np.array_equal(np.isfinite(gt), mine)
+        np.testing.assert_allclose(gt[mine], Z[mine, tg[mine] - a], rtol=0, atol=1e-5)
+    wsc = D.alloc_workspace(D.DPO_OP_SHARD_COMBINE, R, T, 0, V, dev)
+    g = dict(logp_sum=torch.empty(R, dtype=torch.float32, device=dev),
+             logp_sum64=torch.empty(R, dtype=torch.float64, device=dev),
+             lse=torch.empty(R, T, dtype=torch.float32, device=dev),
+             n_tokens=torch.empty(R, dtype=torch.int32, device=dev))
+    D.dpo_shard_combine(pmax, psum, ptgt, d["targets"], d["mask"], V, g["logp_sum"], g["logp_sum64"], g["lse"],
+                        g["n_tokens"], workspace=wsc)
+    D.dpo_device_status(wsc)
+    _check_forward(x, g, gold)
+
+    pi = gold["logp_sum"]
+    ol = O.dpo_loss(pi, pi + x.ref_noise, x.beta, x.layout)
+    weight = torch.from_numpy(ol["weight"].astype(np.float32)).to(dev)
+    lse_flat = np.zeros(R * T)
+    lse_flat[idx] = gold["lse"]
+    Hc = O.bf16_to_f64(x.hidden.reshape(R * T, H)[idx])
+    for s in (0, S - 1):
+        a, b = cuts[s], cuts[s + 1]
+        ws = D.alloc_workspace(D.DPO_OP_HEAD_BACKWARD, R, T, H, b - a, dev)
+        dh = torch.full((R, T, H), float("nan"), dtype=torch.float32, device=dev)
+        dw = torch.full((b - a, H), float("nan"), dtype=torch.float32, device=dev)
+        D.dpo_head_backward_shard(d["hidden"], d["w"][a:b].contiguous(), d["targets"], d["mask"], a, V, g["lse"],
+                                  weight, dh, dw, 0, workspace=ws)
+        D.dpo_device_status(ws)
+        del ws
+        assert torch.count_nonzero(dh[torch.from_numpy(~m).to(dev)]).item() == 0
+        # the shard's part of dHidden at sampled positions: sum over its rows of D W
+        P = np.exp(hs @ W64[a:b].T - lse_flat[pos][:, None])
+        mine = (tg >= a) & (tg < b)
+        P[np.flatnonzero(mine), tg[mine] - a] -= 1.0
+        dh_want = (ol["weight"][pos // T][:, None] * P) @ W64[a:b]
+        dh_got = np_(dh.view(R * T, H)[torch.from_numpy(pos).to(dev)])
+        # dW rows of the shard: its first and last rows and random ones
+        vs = np.unique(np.concatenate([[a, a + 1, b - 1], rng.choice(np.arange(a, b), size=8, replace=False)]))
+        Ps = np.exp(Hc @ W64[vs].T - gold["lse"][:, None])
+        Ps -= (x.targets.reshape(-1)[idx][:, None] == vs[None, :])
+        dw_want = (ol["weight"][idx // T][:, None] * Ps).T @ Hc
+        dw_got = np_(dw[torch.from_numpy(vs - a).to(dev)])
+        e_dh, e_dw = rel_l2(dh_got, dh_want), rel_l2(dw_got, dw_want)
+        print(f"  shard {s}: rel L2 dHidden {e_dh:.3e}  dW {e_dw:.3e}", flush=True)
+        assert e_dh <= GRAD_REL_L2 and e_dw <= GRAD_REL_L2
+
+
+def test_full_size_logit_sums_workload2():
+    """The forward's logit sums at the 8B head's size through an identity that
+    holds at any size: the sum over the vocabulary of z = W h is (sum of W's
+    rows) . h, so a row's sum is that vector dotted with the sum of its
+    completion hidden states."""
+    dev = need_gpu()
+    print("[gpu] full-size logit sums, workload 2", flush=True)
+    x = W.make_workload(2)
+    d = dev_inputs(x, dev)
+    R, T, H, V = x.rows, x.T, x.H, x.V
+    ws = D.alloc_workspace(D.DPO_OP_SEQ_LOGPS_METRICS, R, T, H, V, dev)
+    ls = torch.empty(R, dtype=torch.float32, device=dev)
+    zs = torch.full((R,), float("nan"), dtype=torch.float64, device=dev)
+    D.dpo_seq_logps_metrics(d["hidden"], d["w"], d["targets"], d["mask"], ls, zs, workspace=ws)
+    D.dpo_device_status(ws)
+    wsum = np.zeros(H)
+    for s in range(0, V, 8192):
+        wsum += O.bf16_to_f64(x.w_vocab[s:s + 8192]).sum(axis=0)
+    m = x.mask != 0
+    want = np.array([O.bf16_to_f64(x.hidden[r][m[r]]).sum(axis=0) @ wsum for r in range(R)])
+    # scale: the sum of |z| over a row's logits, estimated from sampled positions
+    rng = np.random.default_rng(2003)
+    W64 = O.bf16_to_f64(x.w_vocab)
+    scale = np.empty(R)
+    for r in range(R):
+        ts = rng.choice(np.flatnonzero(m[r]), size=8, replace=False)
+        scale[r] = np.abs(O.bf16_to_f64(x.hidden[r][ts]) @ W64.T).sum(axis=1).mean() * m[r].sum()
+    got = np_(zs)
+    print(f"  max |d logit sum| / scale = {np.max(np.abs(got - want) / scale):.3e}", flush=True)
+    assert np.all(np.abs(got - want) <= 1e-5 * scale), (got, want)
