@@ -274,3 +274,47 @@ def test_full_size_logit_sums_workload2():
     got = np_(zs)
     print(f"  max |d logit sum| / scale = {np.max(np.abs(got - want) / scale):.3e}", flush=True)
     assert np.all(np.abs(got - want) <= 1e-5 * scale), (got, want)
+
+
+def test_full_size_f32_logits_workload5():
+    """The fp32-logits path at the materialised-logits workload's shape: the
+    bf16 logits widened to fp32 (exactly) must reproduce the stored oracle
+    sums and lse of those same values, and dlogits at sampled positions."""
+    dev = need_gpu()
+    print("[gpu] full-size fp32 logits, workload 5 shape", flush=True)
+    gold = _golden(5)
+    x = W.make_workload(5)
+    assert _digest(x) == str(gold["digest"])
+    d = dev_inputs(x, dev)
+    R, T, V = x.rows, x.T, x.V
+    lf = d["logits"].float()  # exact: every bf16 value is an fp32 value
+    del d["logits"]
+    torch.cuda.empty_cache()
+    ws = D.alloc_workspace(D.DPO_OP_LOGITS_SEQ_LOGPS, R, T, 0, V, dev)
+    g = dict(logp_sum=torch.empty(R, dtype=torch.float32, device=dev),
+             logp_sum64=torch.empty(R, dtype=torch.float64, device=dev),
+             lse=torch.empty(R, T, dtype=torch.float32, device=dev),
+             n_tokens=torch.empty(R, dtype=torch.int32, device=dev))
+    D.dpo_logits_f32_seq_logps(lf, d["targets"], d["mask"], g["logp_sum"], g["logp_sum64"], g["lse"],
+                               g["n_tokens"], workspace=ws)
+    D.dpo_device_status(ws)
+    _check_forward(x, g, gold)
+    pi = gold["logp_sum"]
+    ol = O.dpo_loss(pi, pi + x.ref_noise, x.beta, x.layout)
+    weight = torch.from_numpy(ol["weight"].astype(np.float32)).to(dev)
+    wsb = D.alloc_workspace(D.DPO_OP_LOGITS_BACKWARD, R, T, 0, V, dev)
+    dl = torch.full((R, T, V), float("nan"), dtype=torch.float32, device=dev)
+    D.dpo_logits_f32_backward(lf, d["targets"], d["mask"], g["lse"], weight, dl, workspace=wsb)
+    D.dpo_device_status(wsb)
+    m = x.mask != 0
+    assert torch.count_nonzero(dl[torch.from_numpy(~m).to(dev)]).item() == 0
+    lse_flat = np.zeros(R * T)
+    lse_flat[np.flatnonzero(m.reshape(-1))] = gold["lse"]
+    rng = np.random.default_rng(1006)
+    pos = np.sort(rng.choice(np.flatnonzero(m.reshape(-1)), size=24, replace=False))
+    want = O.logits_backward_rows(x.logits, x.targets, x.mask, lse_flat.reshape(R, T), ol["weight"], pos)
+    got = np_(dl.view(R * T, V)[torch.from_numpy(pos).to(dev)]).astype(np.float64)
+    e = rel_l2(got, want)
+    print(f"  dlogits rel L2 = {e:.3e}", flush=True)
+    assert e <= GRAD_REL_L2
+    assert np.all(np.abs(got - want) <= 1e-6 * np.abs(ol["weight"]).max() + 2e-4 * np.abs(want))
