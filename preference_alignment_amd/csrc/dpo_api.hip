@@ -214,9 +214,12 @@ hipError_t timed(const char* name, hipStream_t s, F f) {
     on = g_prof_on;
   }
   if (!on) return f();
+  // timing-only events: no system-scope fence (an L2 write-back and
+  // invalidate) when they are recorded, which would otherwise sit between the
+  // timed kernels and slow the work that follows
   hipEvent_t a, b;
-  if (hipEventCreate(&a) != hipSuccess) return hipErrorUnknown;
-  if (hipEventCreate(&b) != hipSuccess) {
+  if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess) return hipErrorUnknown;
+  if (hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
     hipEventDestroy(a);
     return hipErrorUnknown;
   }
