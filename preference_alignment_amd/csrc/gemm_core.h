@@ -10,24 +10,29 @@
 //
 // Block tile 256x256x64, 512 threads = 8 waves in a 2x4 grid (two waves per
 // SIMD, so one wave's LDS and barrier waits are covered by the other's MFMAs);
-// each wave owns a 128x64 sub-tile held as 4x2 fragments of
-// v_mfma_f32_32x32x16_bf16 (128 accumulator registers).  Operand tiles go
-// from global memory straight into LDS with buffer_load_dwordx4 ... lds
-// (global_load_lds_dwordx4 for dHidden; 16 bytes per lane, no register
-// staging), double buffered (2 stages x 2 operands x
-// 32 KiB = 128 KiB of the 160 KiB LDS).  The K loop is software pipelined:
-// the fragments of the next 16-wide K step are read while the MFMAs of the
-// current one issue, and the stage barrier sits inside the MFMA stream of the
-// last step of a stage, with the next stage's first fragments read across it.
+// each wave owns a 128x64 sub-tile held as 8x4 fragments of
+// v_mfma_f32_16x16x32_bf16 (128 accumulator registers).  With random bf16
+// data the part runs power-limited, and the 16x16x32 form moves half the
+// accumulator bytes per flop of the 32x32x16 one: the same loop built on
+// 32x32x16 sustained ~1.8 GHz and ran 5-8 % slower than this one (~2.0 GHz).
+// Operand tiles go from global memory straight into LDS with
+// buffer_load_dwordx4 ... lds (16 bytes per lane, no register staging; the
+// flat global_load_lds form also counts on the LDS counter, which forces the
+// compiler to wait for every fragment read), double buffered (2 stages x 2 operands x
+// 32 KiB = 128 KiB of the 160 KiB LDS).  A stage (64 K values) is two 32-wide
+// K steps.  The loop is software pipelined one step ahead: while the MFMAs of
+// one step issue row by row, each fragment of the next step is read into the
+// registers of a fragment the current step has finished with, and the stage
+// barrier sits after the first row of a stage's second step.
 //
 // Both loads place lane L's 16 bytes at (wave base + 16 L), so the LDS
 // swizzles below are realised by choosing which global chunk each lane fetches.
 //
-// MFMA 32x32x16 register layout (CDNA3/CDNA4 32x32 family): lane l supplies
-// A[l % 32][8 (l / 32) + 0..7] and B^T likewise; accumulator element e of lane
-// l is C[8 (e / 4) + 4 (l / 32) + (e % 4)][l % 32].  The K permutation inside
-// a fragment is irrelevant (A and B use the same one); the C layout is what the
-// epilogues rely on.
+// MFMA 16x16x32 register layout (CDNA4): lane l supplies A[l % 16][8 (l / 16)
+// + 0..7] and B^T likewise; accumulator element e of lane l is
+// C[4 (l / 16) + e][l % 16].  The K permutation inside a fragment is
+// irrelevant (A and B use the same one); the C layout is what the epilogues
+// rely on.
 #pragma once
 
 #include "dpo_common.h"
@@ -40,9 +45,11 @@ constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int NTHREADS = 512;
 constexpr int WAVES_N = 4;             // waves along the MFMA columns
-constexpr int FM = 4;                  // 32-row fragments per wave (128 rows)
-constexpr int FN = 2;                  // 32-col fragments per wave (64 cols)
-constexpr int WAVE_COLS = 32 * FN;
+constexpr int FRAG = 16;               // rows / columns of one MFMA fragment
+constexpr int FM = 8;                  // row fragments per wave (128 rows)
+constexpr int FN = 4;                  // column fragments per wave (64 cols)
+constexpr int ACC_N = 4;               // accumulator elements per lane and fragment
+constexpr int WAVE_COLS = FRAG * FN;
 constexpr int OPER_BYTES = BM * BK * 2;       // 32 KiB
 constexpr int STAGE_BYTES = 2 * OPER_BYTES;   // A + B
 constexpr int PIPE_BYTES = 2 * STAGE_BYTES;   // double buffer, 128 KiB
@@ -53,7 +60,7 @@ constexpr int NUM_XCD = 8;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct Acc {
-  floatx16 c[FM][FN];
+  floatx4 c[FM][FN];
 };
 
 // LDS layout of an operand tile (rows of the MFMA dimension, 64 K values
@@ -89,21 +96,6 @@ __device__ __forceinline__ RowOperand row_operand(const uint16_t* base, size_t l
 __device__ __forceinline__ int row_lchunk(int tid) { return (tid & 7) ^ ((tid >> 4) & 7); }
 __device__ __forceinline__ int row_loader_row(int it, int tid) { return it * LOADER_ROW_STRIDE + (tid >> 3); }
 
-// ROW operand read with global_load_lds from per-row 64-bit pointers.  Same
-// LDS layout as RowOperand; measured faster than buffer loads for the
-// dHidden contraction, whose two operands both stride 256 KiB between rows.
-struct FlatRowOperand {
-  const uint16_t* rows[LOADS_PER_THREAD];  // element (row, lchunk * 8) at K = 0
-};
-
-__device__ __forceinline__ void load_stage(const FlatRowOperand& op, int kstep, char* lds_tile, int wave) {
-#pragma unroll
-  for (int it = 0; it < LOADS_PER_THREAD; ++it) {
-    lds_ptr_t dst = (lds_ptr_t)(lds_tile + (it * NTHREADS + wave * 64) * 16);
-    __builtin_amdgcn_global_load_lds((const void*)(op.rows[it] + (size_t)kstep * BK), dst, 16, 0, 0);
-  }
-}
-
 __device__ __forceinline__ void load_stage(const RowOperand& op, int kstep, char* lds_tile, int wave) {
   const unsigned soff = __builtin_amdgcn_readfirstlane((unsigned)kstep * BK * 2);
 #pragma unroll
@@ -117,52 +109,72 @@ __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)"
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr;
 
-// Fragment readers.  `f` = fragment index along the MFMA dimension (32 wide),
-// `base` = first MFMA row/column of this wave inside the tile, kk = 16-wide K step.
+// Fragment reader.  `f` = fragment index along the MFMA dimension (16 wide),
+// `base` = first MFMA row/column of this wave inside the tile, s = 32-wide K
+// step inside the stage.  Lanes 16 q .. 16 q + 15 read the 16-byte chunk
+// 4 s + q of 16 consecutive rows: with the swizzle above, each group of 16
+// lanes covers all 64 banks once.
 struct RowFrag {
-  int off[4];  // byte offset of (row, chunk of step kk) for fragment 0
+  int off[2];  // byte offset of (row, chunk of step s) for fragment 0
   __device__ __forceinline__ void init(int base, int lane) {
-    const int sw = (lane >> 1) & 7;
+    const int sw = ((lane & 15) >> 1) & 7;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) off[kk] = (base + (lane & 31)) * 128 + (((2 * kk + (lane >> 5)) ^ sw) << 4);
+    for (int s = 0; s < 2; ++s) off[s] = (base + (lane & 15)) * 128 + (((4 * s + (lane >> 4)) ^ sw) << 4);
   }
-  __device__ __forceinline__ bf16x8_t read(const char* tile, int f, int kk) const {
-    return *(const bf16x8_t*)(tile + off[kk] + f * 4096);
+  __device__ __forceinline__ bf16x8_t read(const char* tile, int f, int s) const {
+    return *(const bf16x8_t*)(tile + off[s] + f * FRAG * 128);
   }
 };
 
-template <typename Op, int NF> struct FragOf;
-template <int NF> struct FragOf<RowOperand, NF> { typedef RowFrag type; };
-template <int NF> struct FragOf<FlatRowOperand, NF> { typedef RowFrag type; };
-
 // The K loop over nk steps of BK.  nk may be 0 (accumulators stay zero).  The
 // R operand supplies the MFMA rows (wave (wm, wn) owns rows wm*128 .. +128),
-// the C operand the MFMA columns (columns wn*64 .. +64).  Software pipelined:
-// the fragments of the next 16-wide K step are read while the MFMAs of the
-// current one issue, and the stage barrier sits inside the MFMA stream of the
-// last step of a stage, with the next stage's first fragments read across it.
+// the C operand the MFMA columns (columns wn*64 .. +64).
+//
+// Fragments live in two slots; a step's MFMAs run row by row (row i = the FN
+// MFMAs that use A_i), and right behind row i the next step's B_i (i < FN)
+// and A_i are read into the other slot, so A is held about once and only B
+// twice (128 accumulator + ~72 fragment registers).  Each row is a scheduling
+// region of its own with a fixed MFMA / LDS-read interleave.  Per stage: step
+// 0 on slot 0 (reading step 1 into slot 1); row 0 of step 1; the stage
+// barrier (the next stage's tiles have landed, every wave is done reading
+// this stage's buffer); the loads two stages ahead into that buffer; rows
+// 1..7 of step 1, reading the next stage's step 0 into slot 0.  On the last
+// stage those reads fetch unused values from the idle buffer, which keeps
+// the loop free of branches inside the MFMA stream.
 template <typename ROp, typename COp>
 __device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& cop, int nk, char* smem, int wave,
                                          int lane, int wm, int wn) {
+  static_assert(FN <= FM, "B fragments are read behind the first FN rows");
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc.c[i][j][e] = 0.f;
+      for (int e = 0; e < ACC_N; ++e) acc.c[i][j][e] = 0.f;
   if (nk <= 0) return;
 
-  typename FragOf<ROp, FM>::type rf;
-  typename FragOf<COp, FN>::type cf;
+  RowFrag rf, cf;
   rf.init(wm * 128, lane);
   cf.init(wn * WAVE_COLS, lane);
   bf16x8_t fa[2][FM], fb[2][FN];
-#define DPO_READ_FRAGS(stage_, kk_, slot_)                                                     \
-  do {                                                                                         \
-    const char* base_ = smem + (stage_) * STAGE_BYTES;                                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < FM; ++i_) fa[slot_][i_] = rf.read(base_, i_, kk_); \
-    _Pragma("unroll") for (int j_ = 0; j_ < FN; ++j_) fb[slot_][j_] =                          \
-        cf.read(base_ + OPER_BYTES, j_, kk_);                                                  \
+#define DPO_RD_A(buf_, s_, slot_, i_) fa[slot_][i_] = rf.read(smem + (buf_) * STAGE_BYTES, i_, s_)
+#define DPO_RD_B(buf_, s_, slot_, j_) fb[slot_][j_] = cf.read(smem + (buf_) * STAGE_BYTES + OPER_BYTES, j_, s_)
+#define DPO_ROW(slot_, i_, buf_, s_)                                                                      \
+  do {                                                                                                    \
+    _Pragma("unroll") for (int j_ = 0; j_ < FN; ++j_) acc.c[i_][j_] =                                     \
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[slot_][i_], fb[slot_][j_], acc.c[i_][j_], 0, 0, 0);    \
+    if ((i_) < FN) DPO_RD_B(buf_, s_, (slot_) ^ 1, i_);                                                   \
+    DPO_RD_A(buf_, s_, (slot_) ^ 1, i_);                                                                  \
+    if ((i_) < FN) {                                                                                      \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                  \
+    } else {                                                                                              \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                  \
+    }                                                                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                                    \
   } while (0)
 
   load_stage(rop, 0, smem, wave);
@@ -173,51 +185,38 @@ __device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& co
     load_stage(rop, 1, smem + STAGE_BYTES, wave);
     load_stage(cop, 1, smem + STAGE_BYTES + OPER_BYTES, wave);
   }
-  DPO_READ_FRAGS(0, 0, 0);
+  // the loop's own read order (B_i, A_i, ...), all landed before the loop: the
+  // compiler's wait counts at the loop head then follow the loop's reads only
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    if (i < FN) DPO_RD_B(0, 0, 0, i);
+    DPO_RD_A(0, 0, 0, i);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int sl = kk & 1;
-      if (kk < 3) {
-        if (sl)
-          DPO_READ_FRAGS(cur, kk + 1, 0);
-        else
-          DPO_READ_FRAGS(cur, kk + 1, 1);
+    for (int i = 0; i < FM; ++i) DPO_ROW(0, i, cur, 1);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][i], fb[sl][j], acc.c[i][j], 0, 0, 0);
-        // one fragment read between consecutive MFMAs
-#pragma unroll
-        for (int u = 0; u < FM + FN; ++u) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      } else {
-        // last 16-wide step of the stage: 2 MFMAs, the stage barrier, the next
-        // stage's loads and first fragments, then the remaining MFMAs
-        acc.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][0], fb[1][0], acc.c[0][0], 0, 0, 0);
-        acc.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][0], fb[1][1], acc.c[0][1], 0, 0, 0);
-        if (kt + 1 < nk) {
-          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-          __builtin_amdgcn_s_barrier();
-          if (kt + 2 < nk) {
-            load_stage(rop, kt + 2, smem + cur * STAGE_BYTES, wave);
-            load_stage(cop, kt + 2, smem + cur * STAGE_BYTES + OPER_BYTES, wave);
-          }
-          DPO_READ_FRAGS(cur ^ 1, 0, 0);
-        }
-#pragma unroll
-        for (int u = 2; u < FM * FN; ++u)
-          acc.c[u / FN][u % FN] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][u / FN], fb[1][u % FN], acc.c[u / FN][u % FN], 0, 0, 0);
-      }
+    for (int j = 0; j < FN; ++j)
+      acc.c[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[1][0], fb[1][j], acc.c[0][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < nk) {
+      load_stage(rop, kt + 2, smem + cur * STAGE_BYTES, wave);
+      load_stage(cop, kt + 2, smem + cur * STAGE_BYTES + OPER_BYTES, wave);
     }
+    DPO_RD_B(cur ^ 1, 0, 0, 0);
+    DPO_RD_A(cur ^ 1, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 1; i < FM; ++i) DPO_ROW(1, i, cur ^ 1, 0);
   }
-#undef DPO_READ_FRAGS
+#undef DPO_ROW
+#undef DPO_RD_B
+#undef DPO_RD_A
   // every wave is done with the LDS tiles before the caller reuses them
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __syncthreads();
@@ -226,9 +225,9 @@ __device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& co
 // Row (within the 256-row block tile) and column (within the 256-col tile) of
 // accumulator element e of fragment (i, j) for this lane.
 __device__ __forceinline__ int acc_row(int wm, int i, int e, int lane) {
-  return wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+  return wm * 128 + i * FRAG + 4 * (lane >> 4) + e;
 }
-__device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * WAVE_COLS + j * 32 + (lane & 31); }
+__device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * WAVE_COLS + j * FRAG + (lane & 15); }
 
 // Persistent tile scheduler.  Tiles are numbered in grouped order (GM m-tiles
 // wide, m fastest, then n) and the numbering is cut into NUM_XCD contiguous

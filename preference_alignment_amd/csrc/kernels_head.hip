@@ -124,11 +124,11 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CompactArgs a) {
 // forward contraction with the online log-sum-exp epilogue
 // ---------------------------------------------------------------------------
 // The MFMA runs with exchanged roles (rows = vocabulary, columns = positions):
-// a lane then holds one position and 64 of the wave's 128 vocabulary entries,
-// the other 64 sitting in lane ^ 32.  The per-position max and sum of
-// exponentials over the wave's columns are in-lane reductions plus one
-// cross-half shuffle, and the two vocabulary halves of the block (wm = 0, 1)
-// meet through a small LDS table.
+// a lane then holds one position and 32 of the wave's 128 vocabulary entries,
+// the other 96 sitting in lanes ^ 16, ^ 32 and ^ 48.  The per-position max
+// and sum of exponentials over the wave's rows are in-lane reductions plus
+// two cross-lane shuffles, and the two vocabulary halves of the block
+// (wm = 0, 1) meet through a small LDS table.
 constexpr int kEpiBytes = 8192;  // per-position staging + cross-wave reduction
 
 template <typename F>
@@ -136,7 +136,7 @@ __device__ __forceinline__ void for_vocab(const Acc& acc, int j, F f) {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) f(acc.c[i][j][e]);
+    for (int e = 0; e < ACC_N; ++e) f(acc.c[i][j][e]);
 }
 
 // The lane / thread index through an empty asm: offsets computed from it in an
@@ -156,8 +156,8 @@ __device__ __forceinline__ void mask_vocab_tail(Acc& acc, int vbase, int V, int 
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (vbase + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3) >= V) acc.c[i][j][e] = -INFINITY;
+      for (int e = 0; e < ACC_N; ++e)
+        if (vbase + i * FRAG + 4 * (lane >> 4) + e >= V) acc.c[i][j][e] = -INFINITY;
 }
 
 template <bool ZSUM>
@@ -197,45 +197,45 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
       const int pl = acc_col(wn, j, lane);  // position within the tile
       float mx = -INFINITY;
       for_vocab(acc, j, [&](float v) { mx = fmaxf(mx, v); });
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // a lane pair whose rows are all past V keeps (-inf, 0)
+      // a lane group whose rows are all past V keeps (-inf, 0)
       const float ml = mx == -INFINITY ? 0.f : mx * kLog2e;
       float s = 0.f;
       for_vocab(acc, j, [&](float v) { s += fast_exp2(fmaf(v, kLog2e, -ml)); });
+      s += __shfl_xor(s, 16, 64);
       s += __shfl_xor(s, 32, 64);
       if (ZSUM) {
         float zs = 0.f;
         for_vocab(acc, j, [&](float v) { zs += v == -INFINITY ? 0.f : v; });
+        zs += __shfl_xor(zs, 16, 64);
         zs += __shfl_xor(zs, 32, 64);
-        if (lane < 32) red_z[wm * 256 + pl] = zs;
+        if (lane < 16) red_z[wm * 256 + pl] = zs;
       }
       const int off = tgt_s[pl] - vbase;
       if (off >= 0 && off < 128) {
-        const int r = off & 31;
-        if (((r >> 2) & 1) == (lane >> 5) && m0 + pl < n_c) {
-          const int ii = off >> 5, ee = ((r >> 3) << 2) | (r & 3);
-          // acc.c[ii][j][ee] through a select tree on the index bits (6 lane
+        const int r = off & 15;
+        if ((r >> 2) == (lane >> 4) && m0 + pl < n_c) {
+          const int ii = off >> 4, ee = r & 3;
+          // acc.c[ii][j][ee] through a select tree on the index bits (5 lane
           // masks in all, instead of one per candidate element)
           float vi[FM];
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
-            float t[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) t[e] = acc.c[i][j][e];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const bool hi = (ee >> b) & 1;
-#pragma unroll
-              for (int k = 0; k < (16 >> (b + 1)); ++k) t[k] = hi ? t[2 * k + 1] : t[2 * k];
-            }
-            vi[i] = t[0];
+            const float t0 = (ee & 1) ? acc.c[i][j][1] : acc.c[i][j][0];
+            const float t1 = (ee & 1) ? acc.c[i][j][3] : acc.c[i][j][2];
+            vi[i] = (ee & 2) ? t1 : t0;
           }
-          const float v01 = (ii & 1) ? vi[1] : vi[0];
-          const float v23 = (ii & 1) ? vi[3] : vi[2];
-          a.tgt_logit[m0 + pl] = (ii & 2) ? v23 : v01;
+#pragma unroll
+          for (int b = 0; b < 3; ++b) {
+            const bool hi = (ii >> b) & 1;
+#pragma unroll
+            for (int k = 0; k < (FM >> (b + 1)); ++k) vi[k] = hi ? vi[2 * k + 1] : vi[2 * k];
+          }
+          a.tgt_logit[m0 + pl] = vi[0];
         }
       }
-      if (lane < 32) red[wm * 256 + pl] = make_float2(mx, s);
+      if (lane < 16) red[wm * 256 + pl] = make_float2(mx, s);
     }
     __syncthreads();
     if (tid < BM) {
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(256) void k_gather_ht(GatherHTArgs a) {
 // ---------------------------------------------------------------------------
 // Same MFMA orientation as the forward (rows = vocabulary, columns =
 // positions): a lane holds 4 consecutive vocabulary entries of one position
-// per accumulator group, packed to one 8-byte LDS write.  The bf16 tile (256
+// per fragment, packed to one 8-byte LDS write.  The bf16 tile (256
 // positions x 256 vocabulary, 128 KiB) is staged in the freed pipeline LDS
 // and leaves as 16-byte coalesced rows of D [Mp, Vp] and of D^T [Vp, Mp].
 // Staging layout: the 16-byte chunk c of position row p sits at chunk
@@ -496,21 +496,19 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
       const float L = lse_s[pl];
       const float wr = w_s[pl];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        const int vl = acc_row(wm, i, 0, elane);  // first of 4 vocabulary rows
+        float d[ACC_N];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int vl = wm * 128 + i * 32 + 8 * q + 4 * (elane >> 5);  // first of 4 vocabulary rows
-          float d[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            // rows past V hold -inf: exp gives 0
-            d[u] = wr * fast_exp2(fmaf(acc.c[i][j][4 * q + u], kLog2e, -L));
-          }
-          uint2 pk;
-          pk.x = pack_bf16x2(d[0], d[1]);
-          pk.y = pack_bf16x2(d[2], d[3]);
-          *(uint2*)(smem + stage_off(pl, vl)) = pk;
+        for (int u = 0; u < ACC_N; ++u) {
+          // rows past V hold -inf: exp gives 0
+          d[u] = wr * fast_exp2(fmaf(acc.c[i][j][u], kLog2e, -L));
         }
+        uint2 pk;
+        pk.x = pack_bf16x2(d[0], d[1]);
+        pk.y = pack_bf16x2(d[2], d[3]);
+        *(uint2*)(smem + stage_off(pl, vl)) = pk;
+      }
     }
     __syncthreads();
     // D rows: position m0+p, vocabulary n0 .. n0+255
@@ -575,23 +573,15 @@ __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
     const int m0 = mt * BM, n0 = nt * BN;
     const int kb = ks * nks;
     const int nk = max(0, min(nks, nkt - kb));
-    FlatRowOperand dop, wop;
-    {
-      const int lchunk = row_lchunk(tid);
-#pragma unroll
-      for (int it = 0; it < LOADS_PER_THREAD; ++it) {
-        const int r = row_loader_row(it, tid);
-        dop.rows[it] = a.D + (size_t)(m0 + r) * a.Vp + (size_t)kb * BK + lchunk * 8;
-        wop.rows[it] = a.wt + (size_t)min(n0 + r, a.H - 1) * a.ldw + (size_t)kb * BK + lchunk * 8;
-      }
-    }
+    const RowOperand dop = row_operand(a.D + (size_t)m0 * a.Vp, a.Vp, (long)a.Mp - m0, kb * BK, tid);
+    const RowOperand wop = row_operand(a.wt + (size_t)n0 * a.ldw, a.ldw, (long)a.H - n0, kb * BK, tid);
     Acc acc;
     mainloop(acc, dop, wop, nk, smem, wave, lane, wm, wn);
     float* part = a.part + (size_t)ks * a.Mp * a.H;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < ACC_N; ++e) {
         const int m = m0 + acc_row(wm, i, e, lane);
         if (m >= n_c) continue;
         float* dst = part + (size_t)m * a.H;
@@ -656,7 +646,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < ACC_N; ++e) {
         const int v = m0 + acc_row(wm, i, e, lane);
         if (v >= a.V) continue;
         float* dst = a.d_w + (size_t)v * a.H;
