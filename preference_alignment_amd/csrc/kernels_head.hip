@@ -533,9 +533,8 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
         const int c0 = u & 63;                      // vocabulary quad
         const int P0 = (u >> 6) * 128 + 32 * grp;   // first position of this lane group
         const int prow = P0 + 8 * (L & 3) + (L >> 2);
-        typedef __attribute__((address_space(3))) i16x4_t* lds_q;
-        const i16x4_t A = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_q)(smem + stage_off(prow, 4 * c0)));
-        const i16x4_t B = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_q)(smem + stage_off(prow + 4, 4 * c0)));
+        const i16x4_t A = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(smem + stage_off(prow, 4 * c0)));
+        const i16x4_t B = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(smem + stage_off(prow + 4, 4 * c0)));
         const int v = 4 * c0 + (L & 3);
         const int P = P0 + 8 * (L >> 2);
         const u32x4 o = {(uint32_t)(uint16_t)A[0] | ((uint32_t)(uint16_t)A[1] << 16),
