@@ -114,6 +114,11 @@ def parse():
     p.add_argument("--cpu-sample-pairs", type=int, default=None,
                    help="pairs in the CPU baseline sample; default 1 for the fused head, 2 for given logits")
     p.add_argument("--no-kernel-timing", action="store_true")
+    p.add_argument("--all-kernel-timing", action="store_true",
+                   help="bracket every kernel with events inside the timed region (default: only the dominant "
+                        "kernel there; the per-kernel breakdown comes from an untimed pass)")
+    p.add_argument("--profile-steps", type=int, default=2,
+                   help="untimed steps with every kernel timed, run before the timed region")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
     p.add_argument("--row", default="main", choices=ROWS,
                    help="main: the fused step (or the streaming step for workload 5); loss-variant: "
@@ -384,7 +389,33 @@ def main():
     for _ in range(a.warmup):
         runner.step()
     torch.cuda.synchronize()
+
+    # the kernels the roofline may name: the contractions, or the two streams
+    sfx = "_f32" if row == "f32-logits" else ""
+    if a.workload == 5:
+        candidates = ["stream_fwd" + sfx, "stream_bwd" + sfx]
+    elif a.workload == 3:
+        candidates = ["fwd_gemm"]
+    else:
+        candidates = ["fwd_gemm", "dlogits_gemm", "dhidden_gemm", "dw_gemm"]
+    kernels, kernels_steps, dom = {}, a.steps, candidates[-1]
     if not a.no_kernel_timing:
+        if a.all_kernel_timing:
+            D.dpo_profile_select(None)
+        else:
+            # an untimed pass with every kernel bracketed by events gives the
+            # per-kernel breakdown and the dominant kernel (the most time per
+            # step); only that kernel carries events in the timed region
+            D.dpo_profile_select(None)
+            D.dpo_profile_enable(True)
+            for _ in range(a.profile_steps):
+                runner.step()
+            torch.cuda.synchronize()
+            kernels, kernels_steps = D.dpo_profile_read(), a.profile_steps
+            D.dpo_profile_enable(False)
+            tot = {k: kernels[k][0] for k in candidates if k in kernels}
+            dom = max(tot, key=tot.get) if tot else candidates[-1]
+            D.dpo_profile_select(dom)
         D.dpo_profile_enable(True)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -397,10 +428,15 @@ def main():
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
     ms = e0.elapsed_time(e1)
-    kernels = {}
+    timed_kernels = {}
     if not a.no_kernel_timing:
-        kernels = D.dpo_profile_read()
+        timed_kernels = D.dpo_profile_read()
         D.dpo_profile_enable(False)
+        D.dpo_profile_select(None)
+        if a.all_kernel_timing:
+            kernels, kernels_steps = timed_kernels, a.steps
+            tot = {k: kernels[k][0] for k in candidates if k in kernels}
+            dom = max(tot, key=tot.get) if tot else candidates[-1]
     ms_step = ms / a.steps
     value = n_c * a.steps / (ms / 1e3)
 
@@ -408,13 +444,13 @@ def main():
     label = str(a.workload) + {"main": "", "f32-logits": " f32", "vocab-shard": " shard4",
                                "loss-variant": " loss-variant", "logits-means": " logits-means"}[row]
     kern_avg = {k: (v[0] / v[1], v[1]) for k, v in kernels.items()}
+    # the dominant kernel's average launch time over the timed region
+    avg = timed_kernels[dom][0] / timed_kernels[dom][1] if dom in timed_kernels else None
+    dom_launches = timed_kernels[dom][1] / a.steps if dom in timed_kernels else 1.0
     if a.workload == 5:
         E = x.rows * x.T * V
         eb = 4.0 if row == "f32-logits" else 2.0
-        sfx = "_f32" if row == "f32-logits" else ""
         per_kernel_bytes = {"stream_fwd" + sfx: n_c * V * eb, "stream_bwd" + sfx: n_c * V * eb + E * eb}
-        dom = max(per_kernel_bytes, key=lambda k: kern_avg.get(k, (0,))[0]) if kern_avg else "stream_bwd" + sfx
-        avg = kern_avg[dom][0] if dom in kern_avg else None
         ach = per_kernel_bytes[dom] / (avg / 1e3) / 1e9 if avg else None
         roof = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": ach / PEAK_HBM_GBS if ach else None,
@@ -422,19 +458,15 @@ def main():
                 "algorithmic_bytes_per_launch": per_kernel_bytes[dom]}
         step_bytes = n_c * V * eb * 2 + E * eb
         extra = {"step_hbm_frac": step_bytes / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS,
-                 "kernels_ms_per_step": {k: round(v[0] / a.steps, 4) for k, v in kernels.items()}}
+                 "kernels_ms_per_step": {k: round(v[0] / kernels_steps, 4) for k, v in kernels.items()}}
     else:
-        gemms = ["fwd_gemm"] if a.workload == 3 else ["fwd_gemm", "dlogits_gemm", "dhidden_gemm", "dw_gemm"]
+        gemms = candidates
         Vw = runner.Vs if row == "vocab-shard" else V
         flops_step = 2.0 * n_c * H * Vw   # each contraction, per step
         # the backward contractions run once per vocabulary slice: the dominant
         # one is the one with the most time per step, and its algorithmic flops
         # per launch are its per-step flops over its launches per step
-        tot = {k: kernels[k][0] for k in gemms if k in kernels}
-        dom = max(tot, key=tot.get) if tot else gemms[0]
-        avg = kern_avg[dom][0] if dom in kern_avg else None
-        launches = kernels[dom][1] / a.steps if dom in kernels else 1.0
-        flops = flops_step / launches
+        flops = flops_step / dom_launches
         ach = flops / (avg / 1e3) / 1e12 if avg else None
         roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS if ach else None,
@@ -444,7 +476,7 @@ def main():
         extra = {"step_mfma_frac": step_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                  "step_useful_mfma_frac": (flops_step * (1 if a.workload == 3 else 3)) / (ms_step / 1e3) / 1e12
                  / PEAK_BF16_TFLOPS,
-                 "kernels_ms_per_step": {k: round(v[0] / a.steps, 4) for k, v in kernels.items()}}
+                 "kernels_ms_per_step": {k: round(v[0] / kernels_steps, 4) for k, v in kernels.items()}}
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -468,6 +500,9 @@ def main():
                    f"one GPU's share of a {shards}-way vocabulary split (V/{shards} = {runner.Vs})"},
         "roofline": roof, "cpu_baseline": cpu,
         "kernels_ms_avg": {k: round(v[0], 4) for k, v in kern_avg.items()},
+        "kernel_timing": None if a.no_kernel_timing else {
+            "events_in_timed_region": "every kernel" if a.all_kernel_timing else dom,
+            "breakdown_from": "timed region" if a.all_kernel_timing else f"{kernels_steps} untimed steps"},
         "host_wall_s": t_host,
     }
     line.update(extra)

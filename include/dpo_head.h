@@ -285,8 +285,13 @@ const char* dpo_strerror(int status);
  * waits for the recorded events and returns the number of distinct kernels
  * seen; dpo_profile_entry() returns, for entry i, the kernel name, the summed
  * duration in milliseconds and the number of launches.  Enabling (on=1) or
- * disabling (on=0) clears what was collected. */
+ * disabling (on=0) clears what was collected.  dpo_profile_select() limits the
+ * timing to the kernels named `name` (the names dpo_profile_entry() reports;
+ * NULL or "" restores all kernels); the string is copied, and the choice holds
+ * until the next call, across enable/disable.  Host-only: it touches no
+ * device and never fails. */
 int dpo_profile_enable(int on);
+int dpo_profile_select(const char* name);
 int dpo_profile_count(void);
 int dpo_profile_entry(int i, const char** name, double* total_ms, int* launches);
 

@@ -173,6 +173,7 @@ struct ProfSum {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+std::string g_prof_only;  // empty: time every kernel
 std::vector<ProfRec> g_prof_pending;
 std::vector<ProfSum> g_prof_sums;
 
@@ -211,7 +212,7 @@ hipError_t timed(const char* name, hipStream_t s, F f) {
   bool on;
   {
     std::lock_guard<std::mutex> g(g_prof_mu);
-    on = g_prof_on;
+    on = g_prof_on && (g_prof_only.empty() || g_prof_only == name);
   }
   if (!on) return f();
   // timing-only events: no system-scope fence (an L2 write-back and
@@ -859,6 +860,12 @@ int dpo_profile_enable(int on) {
   prof_drain_locked();
   prof_clear_locked();
   g_prof_on = on != 0;
+  return DPO_OK;
+}
+
+int dpo_profile_select(const char* name) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_prof_only = name ? name : "";
   return DPO_OK;
 }
 

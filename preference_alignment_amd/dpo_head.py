@@ -66,6 +66,7 @@ _SIGS = {
     "dpo_device_status": (_I, [_P, _P]),
     "dpo_strerror": (ctypes.c_char_p, [_I]),
     "dpo_profile_enable": (_I, [_I]),
+    "dpo_profile_select": (_I, [ctypes.c_char_p]),
     "dpo_profile_count": (_I, []),
     "dpo_profile_entry": (_I, [_I, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                ctypes.POINTER(ctypes.c_int)]),
@@ -483,6 +484,11 @@ def dpo_strerror(status: int) -> str:
 
 def dpo_profile_enable(on: bool) -> None:
     _check(lib().dpo_profile_enable(1 if on else 0))
+
+
+def dpo_profile_select(name: str | None) -> None:
+    """Time only the kernels called `name` while timing is on (None: all)."""
+    _check(lib().dpo_profile_select(None if not name else name.encode()))
 
 
 def dpo_profile_read() -> dict:

@@ -102,6 +102,11 @@ def test_strerror_and_profile_api(L):
     assert D.dpo_profile_read() == {}
     D.dpo_profile_enable(False)
     assert L.dpo_profile_entry(0, None, None, None) == D.DPO_ERR_SHAPE
+    # kernel selection is host state only: any name, then back to all kernels
+    assert L.dpo_profile_select(b"dlogits_gemm") == D.DPO_OK
+    assert L.dpo_profile_select(None) == D.DPO_OK
+    D.dpo_profile_select("fwd_gemm")
+    D.dpo_profile_select(None)
 
 
 def test_binding_rejects_host_tensors(L):

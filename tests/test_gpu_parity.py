@@ -155,6 +155,31 @@ def test_run_to_run_bitwise_deterministic(case):
         assert torch.equal(a, b)
 
 
+def test_profile_select_times_only_the_named_kernel():
+    # the bench brackets only its dominant kernel with events in the timed region
+    dev = need_gpu()
+    x = CASES["ragged_small"]()
+    d = dev_inputs(x, dev)
+    weight = torch.full((x.rows,), 0.01, dtype=torch.float32, device=dev)
+    try:
+        D.dpo_profile_select("dlogits_gemm")
+        D.dpo_profile_enable(True)
+        g = run_forward(x, d, dev)
+        run_backward(x, d, g["lse"], weight, dev)
+        only = D.dpo_profile_read()
+        D.dpo_profile_select(None)
+        D.dpo_profile_enable(True)
+        g = run_forward(x, d, dev)
+        run_backward(x, d, g["lse"], weight, dev)
+        every = D.dpo_profile_read()
+    finally:
+        D.dpo_profile_enable(False)
+        D.dpo_profile_select(None)
+    assert set(only) == {"dlogits_gemm"} and only["dlogits_gemm"][1] >= 1
+    assert {"fwd_gemm", "dlogits_gemm", "dhidden_gemm", "dw_gemm"} <= set(every)
+    assert every["dlogits_gemm"][1] == only["dlogits_gemm"][1]
+
+
 def test_ignored_targets_are_never_read():
     dev = need_gpu()
     x = CASES["ragged_small"]()
