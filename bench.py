@@ -9,9 +9,11 @@ dW_vocab).  Default workload: 4 pairs x 2,048 tokens at H=4096, V=128,256
 variant instead, --workload 3 the offline reference scoring.
 
 Prints one JSON line: throughput in completion tokens/s, the roofline of the
-dominant kernel (per-kernel HIP event timing from the library, on the stream
-the kernels run on), and the CPU oracle timed on a bounded sample of the same
-workload on this host.
+dominant kernel (the library's HIP event timing on the stream the kernels run
+on: only that kernel is bracketed inside the timed region, after two untimed
+steps with every kernel bracketed have picked it and given the per-kernel
+breakdown), and the CPU oracle timed on a bounded sample of the same workload
+on this host.
 """
 from __future__ import annotations
 
