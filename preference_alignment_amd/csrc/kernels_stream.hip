@@ -205,7 +205,13 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_bwd(StreamBwdArgs a, 
     const long p = c / cpr;
     const int v0 = (int)(c - p * cpr) * kBwdChunk;
     u32x4* out = (u32x4*)((E*)a.d_logits + p * a.V);
-    if (a.mask[p] == 0) {
+    // the position's four scalars in one go (all valid at every position), so
+    // a completion chunk waits for one load latency before its row loads
+    const uint8_t mk = a.mask[p];
+    int tg = a.targets[p];
+    const float lse = a.lse[p];
+    const float w = a.weight[p / a.T];
+    if (mk == 0) {
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int u = 0; u < kBwdVecs; ++u) {
@@ -214,13 +220,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_bwd(StreamBwdArgs a, 
       }
       continue;
     }
-    int tg = a.targets[p];
     if (tg < 0 || tg >= a.V) {
       if (tid == 0 && v0 == 0) atomicOr(&a.hdr->status, kStatusTargetRange);
       tg = -1;
     }
-    const float L = a.lse[p] * kLog2e;
-    const float w = a.weight[p / a.T];
+    const float L = lse * kLog2e;
     const int tv = tg >= 0 ? tg / N : -1;  // the one vector holding the target
     const u32x4* row = (const u32x4*)((const E*)a.logits + p * a.V);
     u32x4 buf[kBwdVecs];
