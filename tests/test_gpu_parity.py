@@ -39,6 +39,13 @@ CASES = {
     # 6 add into the dHidden partial slots of slices 1 and 2
     "six_vocab_slices": lambda: _case("six_vocab_slices", seed=106, rows=8, T=4096, H=64, V=90000,
                                       prompt_lo=3400, prompt_hi=3600, w_std=0.25, targets_dist="zipf"),
+    # tile-exact: N_c = 512 (two position tiles), V = 512 (two vocabulary tiles),
+    # H = 256 (four K stages): no ragged edge anywhere
+    "tile_exact": lambda: _case("tile_exact", seed=107, rows=4, T=128, H=256, V=512, prompt_lo=0, prompt_hi=0),
+    # just past the tiles: N_c = 258 (a position tile + 2), V = 264 (a
+    # vocabulary tile + 8 rows, the smallest overhang V % 8 == 0 allows),
+    # H = 128 (two K stages)
+    "tile_plus": lambda: _case("tile_plus", seed=108, rows=2, T=160, H=128, V=264, prompt_lo=31, prompt_hi=31),
     # minimum sizes
     "tiny_min": lambda: _case("tiny_min", seed=104, rows=2, T=3, H=64, V=8, prompt_lo=0, prompt_hi=1,
                               w_std=0.3),
