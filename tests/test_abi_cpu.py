@@ -34,6 +34,13 @@ def test_workspace_sizes(L):
                  (8, 8, 0, 64), (256, 4096, 4096, 128256)]:  # last: hidden tensor of 8 GiB
         assert D.dpo_workspace_bytes(D.DPO_OP_SEQ_LOGPS, *args) == 0, args
     assert D.dpo_workspace_bytes(99, 8, 8, 64, 64) == 0
+    # the edges of the size limits: the hidden tensor (addressed with 32-bit
+    # byte offsets) must stay under 4 GiB, rows*T under 2^31 - 256
+    assert D.dpo_workspace_bytes(D.DPO_OP_SEQ_LOGPS, 2, 65536, 16320, 64) > 0   # 4 GiB - 16 MiB
+    assert D.dpo_workspace_bytes(D.DPO_OP_SEQ_LOGPS, 2, 65536, 16384, 64) == 0  # exactly 4 GiB
+    last = (2 ** 31 - 256) // 2 - 1
+    assert D.dpo_workspace_bytes(D.DPO_OP_LOGITS_SEQ_LOGPS, 2, last, 0, 64) > 0
+    assert D.dpo_workspace_bytes(D.DPO_OP_LOGITS_SEQ_LOGPS, 2, last + 1, 0, 64) == 0
     # logits ops ignore H
     assert D.dpo_workspace_bytes(D.DPO_OP_LOGITS_SEQ_LOGPS, 8, 2048, 0, 128256) > 0
     assert D.dpo_workspace_bytes(D.DPO_OP_LOGITS_BACKWARD, 8, 2048, 0, 128256) == 256
