@@ -769,33 +769,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_targets(SortArgs a) {
 // order and subtracts the total.  The order of every sum is fixed.
 constexpr int kOnehotChunk = 64;
 constexpr int kOnehotCols = 1024;
-constexpr int kOnehotUnroll = 16;
-
-__device__ __forceinline__ float4 onehot_piece(const OnehotDwArgs& a, int j, int e, int c0) {
-  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-  for (; j + kOnehotUnroll <= e; j += kOnehotUnroll) {
-    uint2 hh[kOnehotUnroll];
-#pragma unroll
-    for (int u = 0; u < kOnehotUnroll; ++u) hh[u] = *(const uint2*)(a.hidden + (size_t)a.s_pos[j + u] * a.H + c0);
-#pragma unroll
-    for (int u = 0; u < kOnehotUnroll; ++u) {
-      const float w = a.s_w[j + u];
-      acc0 = fmaf(w, bf16_lo(hh[u].x), acc0);
-      acc1 = fmaf(w, bf16_hi(hh[u].x), acc1);
-      acc2 = fmaf(w, bf16_lo(hh[u].y), acc2);
-      acc3 = fmaf(w, bf16_hi(hh[u].y), acc3);
-    }
-  }
-  for (; j < e; ++j) {
-    const uint2 h = *(const uint2*)(a.hidden + (size_t)a.s_pos[j] * a.H + c0);
-    const float w = a.s_w[j];
-    acc0 = fmaf(w, bf16_lo(h.x), acc0);
-    acc1 = fmaf(w, bf16_hi(h.x), acc1);
-    acc2 = fmaf(w, bf16_lo(h.y), acc2);
-    acc3 = fmaf(w, bf16_hi(h.y), acc3);
-  }
-  return make_float4(acc0, acc1, acc2, acc3);
-}
+constexpr int kOnehotBatch = 8;  // hidden-row loads in flight per thread
 
 __device__ __forceinline__ void sub4(float* dst, float4 v) {
   float4 d = *(float4*)dst;
@@ -806,56 +780,133 @@ __device__ __forceinline__ void sub4(float* dst, float4 v) {
   *(float4*)dst = d;
 }
 
+// The chunk's keys (with the entries on either side), positions and weights
+// are staged in LDS once; the hidden-row loads are then issued a batch at a
+// time, independent of where runs start and end, while each run is still
+// summed entry by entry in ascending order.
 __global__ __launch_bounds__(256) void k_onehot_dw(OnehotDwArgs a) {
+  __shared__ int key_s[kOnehotChunk + 2];  // key_s[t] = keys[i0 - 1 + t]; -2 outside [0, n)
+  __shared__ int pos_s[kOnehotChunk];
+  __shared__ float w_s[kOnehotChunk];
   const int n = a.hdr->n_c;
   const int ch = blockIdx.x;
   const int i0 = ch * kOnehotChunk;
-  const int c0 = blockIdx.y * kOnehotCols + threadIdx.x * 4;
-  if (i0 >= n || c0 >= a.H) return;
+  if (i0 >= n) return;  // the whole block
   const int i1 = min(n, i0 + kOnehotChunk);
-  int i = i0;
-  while (i < i1) {
-    const int k = a.keys[i];
-    int e = i + 1;
-    while (e < i1 && a.keys[e] == k) ++e;
-    const bool starts_here = i > 0 ? a.keys[i - 1] != k : true;
-    const bool ends_here = e < i1 || i1 == n || a.keys[i1] != k;
-    if (k >= 0 && k < a.V) {
-      const float4 v = onehot_piece(a, i, e, c0);
-      if (!starts_here)
-        *(float4*)(a.cont + (size_t)ch * a.H + c0) = v;
-      else if (!ends_here)
-        *(float4*)(a.head + (size_t)ch * a.H + c0) = v;
-      else
-        sub4(a.d_w + (size_t)k * a.H + c0, v);
+  const int m = i1 - i0;
+  const int tid = threadIdx.x;
+  if (tid < kOnehotChunk + 2) {
+    const int i = i0 - 1 + tid;
+    key_s[tid] = (i >= 0 && i < n) ? a.keys[i] : -2;
+  }
+  if (tid < kOnehotChunk) {
+    pos_s[tid] = tid < m ? a.s_pos[i0 + tid] : 0;
+    w_s[tid] = tid < m ? a.s_w[i0 + tid] : 0.f;
+  }
+  __syncthreads();
+  const int c0 = blockIdx.y * kOnehotCols + tid * 4;
+  if (c0 >= a.H) return;
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  bool starts_here = true;  // the current run began in this chunk
+  for (int jb = 0; jb < m; jb += kOnehotBatch) {
+    uint2 hh[kOnehotBatch];
+#pragma unroll
+    for (int u = 0; u < kOnehotBatch; ++u) {
+      const int k = jb + u < m ? key_s[jb + u + 1] : -2;
+      hh[u] = make_uint2(0u, 0u);
+      if (k >= 0 && k < a.V) hh[u] = *(const uint2*)(a.hidden + (size_t)pos_s[jb + u] * a.H + c0);
     }
-    i = e;
+    // runs that start and end in this batch's entries: their dW rows are
+    // updated together after the batch, so the row loads overlap
+    int ek[kOnehotBatch];
+    float4 ev[kOnehotBatch];
+#pragma unroll
+    for (int u = 0; u < kOnehotBatch; ++u) {
+      ek[u] = -1;
+      const int j = jb + u;
+      if (j >= m) continue;
+      const int k = key_s[j + 1];
+      if (k < 0 || k >= a.V) continue;  // no target in this vocabulary range (sorted last)
+      if (key_s[j] != k)
+        starts_here = true;
+      else if (j == 0)
+        starts_here = false;
+      const float w = w_s[j];
+      acc0 = fmaf(w, bf16_lo(hh[u].x), acc0);
+      acc1 = fmaf(w, bf16_hi(hh[u].x), acc1);
+      acc2 = fmaf(w, bf16_lo(hh[u].y), acc2);
+      acc3 = fmaf(w, bf16_hi(hh[u].y), acc3);
+      const bool ends_here = key_s[j + 2] != k;  // the run ends at j (the sentinel covers j = n - 1)
+      if (ends_here || j == m - 1) {
+        const float4 v = make_float4(acc0, acc1, acc2, acc3);
+        if (!starts_here)
+          *(float4*)(a.cont + (size_t)ch * a.H + c0) = v;
+        else if (!ends_here)
+          *(float4*)(a.head + (size_t)ch * a.H + c0) = v;
+        else {
+          ek[u] = k;
+          ev[u] = v;
+        }
+        acc0 = acc1 = acc2 = acc3 = 0.f;
+      }
+    }
+    float4 dv[kOnehotBatch];
+#pragma unroll
+    for (int u = 0; u < kOnehotBatch; ++u)
+      if (ek[u] >= 0) dv[u] = *(const float4*)(a.d_w + (size_t)ek[u] * a.H + c0);
+#pragma unroll
+    for (int u = 0; u < kOnehotBatch; ++u)
+      if (ek[u] >= 0)
+        *(float4*)(a.d_w + (size_t)ek[u] * a.H + c0) =
+            make_float4(dv[u].x - ev[u].x, dv[u].y - ev[u].y, dv[u].z - ev[u].z, dv[u].w - ev[u].w);
   }
 }
 
+// Phase 2, one block per chunk whose last run crosses into the next chunk
+// and starts in it: the block's threads test the following chunk boundaries
+// in parallel to find the chunk where the run ends, then every thread adds
+// head and the cont pieces in chunk order for its 4 columns.
 __global__ __launch_bounds__(256) void k_onehot_dw_join(OnehotDwArgs a) {
+  __shared__ int end_s;
   const int n = a.hdr->n_c;
   const int ch = blockIdx.x;
   const int i0 = ch * kOnehotChunk;
-  const int c0 = blockIdx.y * kOnehotCols + threadIdx.x * 4;
-  if (i0 >= n || c0 >= a.H) return;
+  if (i0 >= n) return;
   const int i1 = min(n, i0 + kOnehotChunk);
   if (i1 == n) return;
   const int k = a.keys[i1 - 1];
   if (a.keys[i1] != k || k < 0 || k >= a.V) return;  // the last run does not cross into the next chunk
-  // the last run must also start in this chunk (otherwise an earlier chunk owns it)
-  int s0 = i1 - 1;
-  while (s0 > i0 && a.keys[s0 - 1] == k) --s0;
-  if (s0 == i0 && i0 > 0 && a.keys[i0 - 1] == k) return;
+  // an earlier chunk owns the run if it already ran through this chunk's start
+  if (i0 > 0 && a.keys[i0] == k && a.keys[i0 - 1] == k) return;
+  const int tid = threadIdx.x;
+  const int nch = (n + kOnehotChunk - 1) / kOnehotChunk;
+  // the first chunk c > ch whose end is the end of the run (every run ends by the last chunk)
+  int last = nch - 1;
+  for (int base = ch + 1; base < nch; base += 256) {
+    if (tid == 0) end_s = nch;
+    __syncthreads();
+    const int c = base + tid;
+    if (c < nch) {
+      const int e = min(n, (c + 1) * kOnehotChunk);
+      if (e == n || a.keys[e] != k) atomicMin(&end_s, c);
+    }
+    __syncthreads();
+    const int found = end_s;
+    __syncthreads();
+    if (found < nch) {
+      last = found;
+      break;
+    }
+  }
+  const int c0 = blockIdx.y * kOnehotCols + tid * 4;
+  if (c0 >= a.H) return;
   float4 t = *(const float4*)(a.head + (size_t)ch * a.H + c0);
-  for (int c = ch + 1; c * kOnehotChunk < n; ++c) {
+  for (int c = ch + 1; c <= last; ++c) {
     const float4 p = *(const float4*)(a.cont + (size_t)c * a.H + c0);
     t.x += p.x;
     t.y += p.y;
     t.z += p.z;
     t.w += p.w;
-    const int e = min(n, (c + 1) * kOnehotChunk);
-    if (e == n || a.keys[e] != k) break;  // the run ends in chunk c
   }
   sub4(a.d_w + (size_t)k * a.H + c0, t);
 }
