@@ -22,9 +22,10 @@ namespace {
 // Tile-group widths (m-tiles per group) of the persistent scheduler.
 constexpr int kGroupFwd = 8;
 constexpr int kGroupBwd = 4;
-// The dHidden contraction has few output tiles (positions x H); splitting its
-// K = vocabulary range in two keeps every CU busy through the last round.
-constexpr int kSplitDh = 2;
+// The dHidden contraction has few output tiles (positions x H): its K =
+// vocabulary range is split in up to this many parts, the count chosen on the
+// device from N_c so that the last round of tiles is nearly full.
+constexpr int kMaxSplitDh = 4;
 // dHidden partial slots are kept for at most this many vocabulary slices;
 // later slices add into slot (slice % kSlotSlices), so the workspace stays
 // linear in the positions when a long batch needs many slices.
@@ -125,7 +126,7 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     L.keysB = take((size_t)L.Mp * 4);
     L.valsB = take((size_t)L.Mp * 4);
     // one fp32 partial per (vocabulary slice, K split): written once, summed by the finish
-    L.dhpart = take((size_t)std::min(L.n_chunks, kSlotSlices) * kSplitDh * L.Mp * H * 4);
+    L.dhpart = take((size_t)std::min(L.n_chunks, kSlotSlices) * kMaxSplitDh * L.Mp * H * 4);
     L.spos = take((size_t)L.Mp * 4);
     L.sw = take((size_t)L.Mp * 4);
     L.ohcont = take((size_t)(L.Mp / 64) * H * 4);
@@ -616,6 +617,8 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
   // dHidden partials (the finish adds them in a fixed order); each slice's dW
   // rows are complete
   float* dh_part = at<float>(ws, L.dhpart);
+  // K steps of the first (widest) slice: the dHidden split count depends on it
+  const int nkt_ref = (int)(align_up((size_t)std::min(V, L.chunk_tiles * gemm::BN), gemm::BN) / gemm::BK);
   for (int c = 0; c < L.n_chunks; ++c) {
     const int v0 = c * L.chunk_tiles * gemm::BN;
     const int Vc = std::min(V - v0, L.chunk_tiles * gemm::BN);
@@ -649,9 +652,10 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
     dh.ldw = L.Vp;
     dh.Mp = L.Mp;
     dh.gm = kGroupBwd;
-    dh.splitk = kSplitDh;
+    dh.max_split = kMaxSplitDh;
+    dh.nkt_ref = nkt_ref;
     dh.hdr = hdr;
-    dh.part = dh_part + (size_t)(c % kSlotSlices) * kSplitDh * L.Mp * H;
+    dh.part = dh_part + (size_t)(c % kSlotSlices) * kMaxSplitDh * L.Mp * H;
     dh.accumulate = c >= kSlotSlices;
     RUN("dhidden_gemm", launch_dh_gemm(dh, persistent_grid(), st));
 
@@ -683,7 +687,10 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
   df.hdr = hdr;
   df.H = H;
   df.Mp = L.Mp;
-  df.splitk = std::min(L.n_chunks, kSlotSlices) * kSplitDh;
+  df.slices = std::min(L.n_chunks, kSlotSlices);
+  df.max_split = kMaxSplitDh;
+  df.nkt_ref = nkt_ref;
+  df.grid = persistent_grid();
   df.d_hidden = d_hidden;
   RUN("dhidden_finish", launch_dh_finish(df, L.Mp, st));
 

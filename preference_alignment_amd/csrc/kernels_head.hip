@@ -549,10 +549,29 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dHidden = D . W  (R = D rows, C = W^T rows), K = vocabulary split in `splitk`
-// parts written as fp32 partials; k_dh_finish adds them in a fixed order,
-// applies the exact one-hot term and scatters rows to their positions.
+// dHidden = D . W  (R = D rows, C = W^T rows), K = the slice's vocabulary
+// split in dh_splits() parts, each written as an fp32 partial; k_dh_finish
+// adds them in a fixed order, applies the exact one-hot term and scatters rows
+// to their positions.
 // ---------------------------------------------------------------------------
+// The dHidden contraction has few output tiles (positions x H), so K (the
+// slice's vocabulary) is split to fill the CUs: the split count minimises
+// rounds of tiles over the grid times K steps per tile (ties to fewer parts).
+// It depends on N_c, which only the device knows; the finish recomputes it.
+__device__ __forceinline__ int dh_splits(int n_c, int H, int nkt, int grid, int max_split) {
+  const long tiles = (long)cdiv(n_c, BM) * cdiv(H, BN);
+  int best = 1;
+  long best_cost = -1;
+  for (int s = 1; s <= max_split && s <= max(nkt, 1); ++s) {
+    const long cost = (tiles * s + grid - 1) / grid * cdiv(nkt, s);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
+
 __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
@@ -562,9 +581,10 @@ __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
   const int n_c = a.hdr->n_c;
   const int nNt = cdiv(a.H, BN);
   const int nkt = a.Vp / BK;
-  const int nks = cdiv(nkt, a.splitk);
+  const int splitk = dh_splits(n_c, a.H, a.nkt_ref, gridDim.x, a.max_split);
+  const int nks = cdiv(nkt, splitk);
   Sched sc;
-  sc.init(cdiv(n_c, BM), nNt * a.splitk, a.gm);
+  sc.init(cdiv(n_c, BM), nNt * splitk, a.gm);
   for (int t = sc.begin; t < sc.end; t += sc.step) {
     int mt, ntk;
     sc.coords(t, mt, ntk);
@@ -603,15 +623,18 @@ __global__ __launch_bounds__(256) void k_dh_finish(DhFinishArgs a) {
   const float wr = tg >= 0 ? a.weight[a.row_c[m]] : 0.f;
   const uint16_t* wrow = a.w + (size_t)(tg >= 0 ? tg : 0) * a.H;
   float* dst = a.d_hidden + (size_t)a.idx[m] * a.H;
+  const int splitk = dh_splits(a.hdr->n_c, a.H, a.nkt_ref, a.grid, a.max_split);
   for (int c = threadIdx.x * 4; c < a.H; c += 256 * 4) {
+    // slice slot by slice slot, split by split
     float4 s = *(const float4*)(a.part + (size_t)m * a.H + c);
-    for (int ks = 1; ks < a.splitk; ++ks) {
-      const float4 p = *(const float4*)(a.part + ((size_t)ks * a.Mp + m) * a.H + c);
-      s.x += p.x;
-      s.y += p.y;
-      s.z += p.z;
-      s.w += p.w;
-    }
+    for (int q = 0; q < a.slices; ++q)
+      for (int ks = q == 0 ? 1 : 0; ks < splitk; ++ks) {
+        const float4 p = *(const float4*)(a.part + ((size_t)(q * a.max_split + ks) * a.Mp + m) * a.H + c);
+        s.x += p.x;
+        s.y += p.y;
+        s.z += p.z;
+        s.w += p.w;
+      }
     const uint2 wv = *(const uint2*)(wrow + c);
     s.x = fmaf(-wr, bf16_lo(wv.x), s.x);
     s.y = fmaf(-wr, bf16_hi(wv.x), s.y);

@@ -126,10 +126,12 @@ struct DProdArgs {
 struct DhArgs {
   const uint16_t* D;    // [Mp, Vp] the slice's D
   const uint16_t* wt;   // [H, ldw] W^T, offset to the slice's first vocabulary column
-  int H, V, Vp, ldw, Mp, gm, splitk;
+  int H, V, Vp, ldw, Mp, gm;
+  int max_split;  // partial slots of the slice; the kernel splits K into dh_splits(...) <= this parts
+  int nkt_ref;    // K steps of the first slice: every slice and the finish choose the same split count
   int accumulate;  // add into the partials (slices beyond the slot count)
   const WsHeader* hdr;
-  float* part;  // [splitk, Mp, H] fp32 partial sums
+  float* part;  // [max_split, Mp, H] fp32 partial sums
 };
 
 struct DhFinishArgs {
@@ -140,7 +142,10 @@ struct DhFinishArgs {
   const int* row_c;
   const float* weight;  // [rows]
   const WsHeader* hdr;
-  int H, Mp, splitk;  // splitk: number of [Mp, H] partial slots to add
+  int H, Mp;
+  int slices;     // slice slots holding partials
+  int max_split;  // partial slots per slice slot
+  int nkt_ref, grid;  // as for k_dh_gemm: the same split count
   float* d_hidden;  // [rows*T, H]
 };
 
