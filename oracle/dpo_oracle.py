@@ -445,14 +445,18 @@ def head_backward(hidden_bits, w_bits, targets, mask, lse, weight, chunk: int = 
                              lse, weight, chunk)
 
 
-def logits_backward_rows(logits_bits, targets, mask, lse, weight, flat_positions) -> np.ndarray:
-    """dlogits [n, V] (float64) for the given flat positions of a [R,T,V] logits input.
+def _dlogits_rows(rows_f64, targets, mask, lse, weight, pos, T, V) -> np.ndarray:
+    """d loss / d logits at flat positions ``pos`` given the logits of those
+    positions as float64 rows [n, V] (``rows_f64(p)`` returns them for a subset
+    p of ``pos``): w_r (softmax - onehot) at completion positions, 0 elsewhere.
 
-    Completion positions get w_r*(softmax - onehot); mask-0 positions get 0.
+    The gradient of the page's hand-written loss over given logits ("DPO
+    Training on GPU, in depth", "A training configuration that fits": log-softmax
+    over the whole vocabulary, gather of the target, masked sum, then the
+    sigmoid loss) is, per completion position t of row r with target y,
+    d loss / d z[t, v] = (d loss / d pi_r) (d pi_r / d z[t, v])
+                       = -w_r ([v == y] - softmax(z_t)[v]).
     """
-    R, T, V = logits_bits.shape
-    pos = np.asarray(flat_positions, dtype=np.int64)
-    lflat = logits_bits.reshape(R * T, V)
     m = np.asarray(mask).reshape(-1) != 0
     tflat = np.asarray(targets).reshape(-1).astype(np.int64)
     lse_flat = np.asarray(lse, dtype=np.float64).reshape(-1)
@@ -461,10 +465,30 @@ def logits_backward_rows(logits_bits, targets, mask, lse, weight, flat_positions
     if live.size:
         p = pos[live]
         _check_targets(tflat[p], V)
-        P = np.exp(bf16_to_f64(lflat[p]) - lse_flat[p][:, None])
+        P = np.exp(rows_f64(p) - lse_flat[p][:, None])
         P[np.arange(p.size), tflat[p]] -= 1.0
         out[live] = _row_weight(weight, p, T)[:, None] * P
     return out
+
+
+def logits_backward_rows_f64(logits, targets, mask, lse, weight, flat_positions) -> np.ndarray:
+    """dlogits [n, V] (float64) at the given flat positions of float64 logits [R,T,V]."""
+    R, T, V = logits.shape
+    lflat = np.asarray(logits, dtype=np.float64).reshape(R * T, V)
+    return _dlogits_rows(lambda p: lflat[p], targets, mask, lse, weight,
+                         np.asarray(flat_positions, dtype=np.int64), T, V)
+
+
+def logits_backward_rows(logits_bits, targets, mask, lse, weight, flat_positions) -> np.ndarray:
+    """dlogits [n, V] (float64) for the given flat positions of a [R,T,V] bf16 logits input.
+
+    Completion positions get w_r*(softmax - onehot); mask-0 positions get 0.
+    Only the requested rows are decoded.
+    """
+    R, T, V = logits_bits.shape
+    lflat = logits_bits.reshape(R * T, V)
+    return _dlogits_rows(lambda p: bf16_to_f64(lflat[p]), targets, mask, lse, weight,
+                         np.asarray(flat_positions, dtype=np.int64), T, V)
 
 
 def head_backward_shard_f64(hidden: np.ndarray, w_shard: np.ndarray, targets: np.ndarray,
@@ -497,23 +521,118 @@ def head_backward_shard_f64(hidden: np.ndarray, w_shard: np.ndarray, targets: np
     return dH.reshape(R, T, H), dW
 
 
-def logits_f32_backward_rows(logits_f32, targets, mask, lse, weight, flat_positions) -> np.ndarray:
-    """As ``logits_backward_rows`` for float32 logits."""
-    R, T, V = logits_f32.shape
+# ----------------------------------------------------------------------------
+# the same quantities at chosen positions or vocabulary rows only: checks at
+# sizes where a whole [N_c, V] or [V, H] float64 array is too large for the host
+# ----------------------------------------------------------------------------
+def _shard_of(w, v_begin, V_total):
+    Vs = w.shape[0]
+    return Vs, (Vs if V_total is None else V_total)
+
+
+def dhidden_rows_f64(hidden: np.ndarray, w: np.ndarray, targets, mask, lse, weight, flat_positions,
+                     v_begin: int = 0, V_total=None) -> np.ndarray:
+    """dHidden [n, H] at the given flat positions of hidden [R,T,H] (float64):
+    sum over the vocabulary rows v of ``w`` (rows [v_begin, v_begin + V_s) of a
+    V_total vocabulary; by default the whole vocabulary) of
+    w_r (softmax(z_t)[v] - [v == y_t]) W[v], with ``lse`` the whole-vocabulary
+    log-sum-exp.  Mask-0 positions get 0.  Per position this is the row of
+    ``head_backward_f64`` (or of ``head_backward_shard_f64`` for a shard)."""
+    R, T, H = hidden.shape
+    Vs, V_total = _shard_of(w, v_begin, V_total)
     pos = np.asarray(flat_positions, dtype=np.int64)
-    lflat = np.asarray(logits_f32, dtype=np.float32).reshape(R * T, V)
     m = np.asarray(mask).reshape(-1) != 0
     tflat = np.asarray(targets).reshape(-1).astype(np.int64)
     lse_flat = np.asarray(lse, dtype=np.float64).reshape(-1)
-    out = np.zeros((pos.size, V))
+    out = np.zeros((pos.size, H))
     live = np.flatnonzero(m[pos])
     if live.size:
         p = pos[live]
-        _check_targets(tflat[p], V)
-        P = np.exp(lflat[p].astype(np.float64) - lse_flat[p][:, None])
-        P[np.arange(p.size), tflat[p]] -= 1.0
-        out[live] = _row_weight(weight, p, T)[:, None] * P
+        _check_targets(tflat[p], V_total)
+        P = np.exp(hidden.reshape(R * T, H)[p] @ w.T - lse_flat[p][:, None])
+        y = tflat[p] - v_begin
+        inside = np.flatnonzero((y >= 0) & (y < Vs))
+        P[inside, y[inside]] -= 1.0
+        out[live] = (_row_weight(weight, p, T)[:, None] * P) @ w
     return out
+
+
+def dw_rows_f64(hidden: np.ndarray, w: np.ndarray, targets, mask, lse, weight, vocab_rows,
+                v_begin: int = 0, V_total=None, chunk: int = 4096) -> np.ndarray:
+    """Rows ``vocab_rows`` (indices into ``w``) of dW_vocab [k, H]: the sum
+    over completion positions t of w_r (softmax(z_t)[v] - [v == y_t]) h_t, as
+    ``head_backward_f64`` (or ``head_backward_shard_f64``) forms it for those rows."""
+    R, T, H = hidden.shape
+    Vs, V_total = _shard_of(w, v_begin, V_total)
+    vs = np.asarray(vocab_rows, dtype=np.int64)
+    idx, _ = completion_positions(mask)
+    tflat = np.asarray(targets).reshape(-1).astype(np.int64)
+    _check_targets(tflat[idx], V_total)
+    hflat = hidden.reshape(R * T, H)
+    lse_flat = np.asarray(lse, dtype=np.float64).reshape(-1)
+    wrow = _row_weight(weight, idx, T)
+    Wv = w[vs]
+    out = np.zeros((vs.size, H))
+    for s in range(0, idx.size, chunk):
+        c = idx[s:s + chunk]
+        Hc = hflat[c]
+        P = np.exp(Hc @ Wv.T - lse_flat[c][:, None])
+        P -= (tflat[c][:, None] - v_begin) == (vs[None, :])
+        out += (wrow[s:s + chunk][:, None] * P).T @ Hc
+    return out
+
+
+def shard_partials_rows_f64(hidden: np.ndarray, w_shard: np.ndarray, targets, mask, v_begin: int,
+                            V_total: int, flat_positions) -> Dict[str, np.ndarray]:
+    """``shard_partials_f64`` at the given flat positions only ([n] arrays)."""
+    R, T, H = hidden.shape
+    Vs = w_shard.shape[0]
+    pos = np.asarray(flat_positions, dtype=np.int64)
+    m = np.asarray(mask).reshape(-1) != 0
+    tflat = np.asarray(targets).reshape(-1).astype(np.int64)
+    pmax = np.full(pos.size, -np.inf)
+    psum = np.zeros(pos.size)
+    ptgt = np.full(pos.size, -np.inf)
+    live = np.flatnonzero(m[pos])
+    if live.size:
+        p = pos[live]
+        _check_targets(tflat[p], V_total)
+        Z = hidden.reshape(R * T, H)[p] @ w_shard.T
+        mx = Z.max(axis=1)
+        pmax[live] = mx
+        psum[live] = np.exp(Z - mx[:, None]).sum(axis=1)
+        y = tflat[p] - v_begin
+        inside = np.flatnonzero((y >= 0) & (y < Vs))
+        ptgt[live[inside]] = Z[inside, y[inside]]
+    return dict(max=pmax, sumexp=psum, tgt=ptgt)
+
+
+def logit_row_sums_by_column_sum(hidden: np.ndarray, w: np.ndarray, mask, chunk: int = 8192) -> np.ndarray:
+    """The per-row logit sums of ``logit_row_sums_f64`` through the identity
+    sum_t sum_v W[v] . h_t = (sum_v W[v]) . (sum_t h_t), which needs no
+    [positions x V] contraction (float64; the order of the additions differs)."""
+    R, T, H = hidden.shape
+    wsum = np.zeros(H)
+    for s in range(0, w.shape[0], chunk):
+        wsum += np.asarray(w[s:s + chunk], dtype=np.float64).sum(axis=0)
+    m = np.asarray(mask) != 0
+    return np.array([hidden[r][m[r]].sum(axis=0) @ wsum for r in range(R)])
+
+
+def logit_abs_sums_f64(hidden: np.ndarray, w: np.ndarray, flat_positions) -> np.ndarray:
+    """sum over the vocabulary of |z| at each given flat position: the scale
+    of the rounding error of any summation of that position's logits."""
+    R, T, H = hidden.shape
+    pos = np.asarray(flat_positions, dtype=np.int64)
+    return np.abs(hidden.reshape(R * T, H)[pos] @ w.T).sum(axis=1)
+
+
+def logits_f32_backward_rows(logits_f32, targets, mask, lse, weight, flat_positions) -> np.ndarray:
+    """As ``logits_backward_rows`` for float32 logits (widened to float64 exactly)."""
+    R, T, V = logits_f32.shape
+    lflat = np.asarray(logits_f32, dtype=np.float32).reshape(R * T, V)
+    return _dlogits_rows(lambda p: lflat[p].astype(np.float64), targets, mask, lse, weight,
+                         np.asarray(flat_positions, dtype=np.int64), T, V)
 
 
 # ----------------------------------------------------------------------------
