@@ -186,15 +186,38 @@ int dpo_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const int
                       const float* weight, float* d_hidden, float* d_w_vocab, int accumulate_dw,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bandwidth-bound variant over pre-materialised logits [rows, T, V] bf16:
- * the same scores as dpo_seq_logps, reading only completion positions. */
+/* Bandwidth-bound variant over pre-materialised logits: the per-token step
+ * of the hand-written chunked loss on "DPO Training on GPU, in depth",
+ * section "A training configuration that fits" (it takes logits and labels,
+ * applies a full-vocabulary log-softmax, gathers the label's entry and sums
+ * over the completion mask), for a caller that already holds the logits
+ * whose size that page's section "Where the memory goes for an 8B model"
+ * works out (0.49 GiB per 2,048-token sequence in bf16 at V = 128,256).
+ *   logits   [rows, T, V] bf16  row-major, 16-byte aligned; read once per
+ *                               completion position, never at mask-0 ones
+ *   targets, mask, rows, T, V, workspace: as dpo_seq_logps (H does not exist
+ *     here; workspace DPO_OP_LOGITS_SEQ_LOGPS)
+ *   logp_sum, logp_sum64, lse, n_tokens: as dpo_seq_logps.
+ * Logits may hold -inf (a caller's vocabulary masking); those entries add
+ * nothing to the log-sum-exp.  A position whose logits are all -inf, or whose
+ * target's logit is -inf, has no finite log-probability. */
 int dpo_logits_seq_logps(const dpo_bf16* logits, const int32_t* targets, const uint8_t* mask,
                          int rows, int T, int V, float* logp_sum, double* logp_sum64, float* lse,
                          int32_t* n_tokens, void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* dlogits [rows, T, V] bf16 (round to nearest even) = weight_r (softmax - onehot)
- * at completion positions and exactly 0 elsewhere. */
+/* Backward of that loss over the given logits (the gradient the page's
+ * chunked loss produces by autograd in "A training configuration that fits";
+ * its section "Where the memory goes for an 8B model" counts this tensor next
+ * to the logits):
+ *   d_logits[r,t,:] = weight_r (softmax(logits[r,t,:]) - onehot(y_{r,t}))
+ * at completion positions, exactly 0 at mask-0 positions, rounded to bf16
+ * (nearest even).
+ *   logits [rows, T, V] bf16; lse [rows, T] float from dpo_logits_seq_logps;
+ *   weight [rows] float from dpo_loss; d_logits [rows, T, V] bf16, written in
+ *   full (16-byte aligned, must not overlap logits).
+ *   workspace: DPO_OP_LOGITS_BACKWARD (a status word only); a target outside
+ *   [0, V) at a completion position is reported by dpo_device_status. */
 int dpo_logits_backward(const dpo_bf16* logits, const int32_t* targets, const uint8_t* mask,
                         int rows, int T, int V, const float* lse, const float* weight,
                         dpo_bf16* d_logits, void* workspace, size_t workspace_bytes,

@@ -85,10 +85,12 @@ __device__ __forceinline__ void absorb(float& m, float& s, const u32x4 v) {
 #pragma unroll
   for (int k = 1; k < N; ++k) lm = fmaxf(lm, x[k]);
   if (lm > m) {
-    s *= fast_exp2((m - lm) * kLog2e);
+    s *= fast_exp2((m - lm) * kLog2e);  // 0 while m is still -inf (s is 0 then too)
     m = lm;
   }
-  const float ml = m * kLog2e;
+  // while every value seen is -inf (logits masked out by the caller), m stays
+  // -inf: a zero shift keeps exp2(-inf) = 0 instead of exp2(-inf + inf) = NaN
+  const float ml = m == -INFINITY ? 0.f : m * kLog2e;
   float acc = 0.f;
 #pragma unroll
   for (int k = 0; k < N; ++k) acc += fast_exp2(fmaf(x[k], kLog2e, -ml));

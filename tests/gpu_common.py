@@ -10,14 +10,16 @@ except ImportError:  # pragma: no cover
 from preference_alignment_amd import dpo_head as D
 
 # Tolerances.  The first three are the stated parity bar of the path; the lse
-# bound is a supplementary check: an fp32 logit from a bf16 x bf16 -> fp32
-# contraction over H <= 4096 is off by ~1e-6, the hardware exp2 by ~1 ulp, so a
-# per-position log-sum-exp within 1e-4 leaves two orders of margin while still
+# bound is a supplementary check: the lse output is fp32 (half an ulp is
+# 9.5e-7 at |lse| in [16, 32)), an fp32 logit from a bf16 x bf16 -> fp32
+# contraction over H <= 4096 is off by ~1e-6 and the hardware exp2 by ~1 ulp,
+# which together move a log-sum-exp over 10^5 terms by ~1e-6 (measured at
+# most 1.5e-6 at the 8B head's full size); 1e-5 keeps that margin while
 # catching a dropped vocabulary tile (which moves lse by ~1e-3 or more).
 LOGP_RTOL = 1e-3       # |d logp_sum| <= 1e-3 * max(1, |sum|)
 LOSS_ATOL = 1e-4       # |d loss|
 GRAD_REL_L2 = 2e-3     # dHidden, dW_vocab, dlogits relative L2 error
-LSE_ATOL = 1e-4
+LSE_ATOL = 1e-5
 WEIGHT_RTOL = 1e-4     # per-row gradient weights (fp32 outputs of an fp64 computation)
 
 

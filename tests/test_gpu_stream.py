@@ -122,3 +122,56 @@ def test_logits_path_deterministic():
     assert torch.equal(a["logp_sum64"], b["logp_sum64"]) and torch.equal(a["lse"], b["lse"])
     w = torch.linspace(-0.1, 0.1, x.rows, dtype=torch.float32, device=dev)
     assert torch.equal(stream_backward(x, d, a["lse"], w, dev), stream_backward(x, d, a["lse"], w, dev))
+
+
+def _minus_inf_case(f32):
+    """Logits the caller has masked to -inf over part of the vocabulary: the
+    first 16-byte vector of the first thread of one position, the first
+    vector of every thread of another (so each thread starts on -inf values),
+    and the vocabulary tail of a third.  Targets sit on finite columns."""
+    x = W.make_logits_inputs(name="minus_inf", logits_dtype="f32" if f32 else "bf16", **CASES["small_ragged"])
+    R, T, V = x.rows, x.T, x.V
+    per_vec = 4 if f32 else 8
+    spans = {(0, 12): (0, per_vec), (1, 20): (0, 256 * per_vec), (3, 39): (V - 40, V), (2, 30): (0, V // 2)}
+    ninf = -np.inf if f32 else np.uint16(0xFF80)
+    for (r, t), (a, b) in spans.items():
+        assert x.mask[r, t] != 0
+        x.logits[r, t, a:b] = ninf
+        x.targets[r, t] = b if b < V else a - 1
+    return x
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_logits_path_minus_inf_columns(f32):
+    dev = need_gpu()
+    print(f"[gpu] logits parity case=minus_inf f32={f32}", flush=True)
+    x = _minus_inf_case(f32)
+    if not f32:
+        _logits_check(x, dev)
+        return
+    R, T, V = x.rows, x.T, x.V
+    d = dict(logits=torch.from_numpy(x.logits).to(dev), targets=torch.from_numpy(x.targets).to(dev),
+             mask=torch.from_numpy(x.mask).to(dev))
+    ws = D.alloc_workspace(D.DPO_OP_LOGITS_SEQ_LOGPS, R, T, 0, V, dev)
+    g = dict(logp_sum=torch.empty(R, dtype=torch.float32, device=dev),
+             logp_sum64=torch.empty(R, dtype=torch.float64, device=dev),
+             lse=torch.empty(R, T, dtype=torch.float32, device=dev),
+             n_tokens=torch.empty(R, dtype=torch.int32, device=dev))
+    D.dpo_logits_f32_seq_logps(d["logits"], d["targets"], d["mask"], g["logp_sum"], g["logp_sum64"], g["lse"],
+                               g["n_tokens"], workspace=ws)
+    D.dpo_device_status(ws)
+    fwd = O.logits_f32_seq_logps(x.logits, x.targets, x.mask)
+    m = x.mask != 0
+    assert np.all(np.isfinite(np_(g["logp_sum64"]))) and np.all(np.isfinite(np_(g["lse"])))
+    assert np.all(np.abs(np_(g["logp_sum64"]) - fwd["logp_sum"]) <= LOGP_RTOL * np.maximum(1.0, np.abs(fwd["logp_sum"])))
+    assert np.max(np.abs(np_(g["lse"])[m] - fwd["lse"][m])) <= LSE_ATOL
+    ol = O.dpo_loss(fwd["logp_sum"], fwd["logp_sum"] + x.ref_noise, x.beta, x.layout)
+    weight = torch.from_numpy(ol["weight"].astype(np.float32)).to(dev)
+    wsb = D.alloc_workspace(D.DPO_OP_LOGITS_BACKWARD, R, T, 0, V, dev)
+    dl = torch.full((R, T, V), float("nan"), dtype=torch.float32, device=dev)
+    D.dpo_logits_f32_backward(d["logits"], d["targets"], d["mask"], g["lse"], weight, dl, workspace=wsb)
+    D.dpo_device_status(wsb)
+    want = O.logits_f32_backward_rows(x.logits, x.targets, x.mask, fwd["lse"], ol["weight"], np.arange(R * T))
+    got = np_(dl).reshape(R * T, V).astype(np.float64)
+    assert rel_l2(got, want) <= GRAD_REL_L2
+    assert np.all(np.abs(got - want) <= 1e-6 * np.abs(ol["weight"]).max() + 2e-4 * np.abs(want))
