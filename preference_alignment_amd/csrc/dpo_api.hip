@@ -24,12 +24,10 @@ constexpr int kGroupFwd = 8;
 constexpr int kGroupBwd = 4;
 // The dHidden contraction has few output tiles (positions x H): its K =
 // vocabulary range is split in up to this many parts, the count chosen on the
-// device from N_c so that the last round of tiles is nearly full.
+// device from N_c so that the last round of tiles is nearly full.  The parts'
+// fp32 slabs take at most 2 Mp x H floats (the device caps the count to fit),
+// and every vocabulary slice adds into the same slabs.
 constexpr int kMaxSplitDh = 4;
-// dHidden partial slots are kept for at most this many vocabulary slices;
-// later slices add into slot (slice % kSlotSlices), so the workspace stays
-// linear in the positions when a long batch needs many slices.
-constexpr int kSlotSlices = 4;
 // The backward holds the bf16 softmax part of dlogits (D and D^T) only for one
 // slice of the vocabulary at a time: each of D and D^T stays under this many
 // bytes (balanced slices of whole 256-wide tiles).
@@ -125,8 +123,9 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     L.valsA = take((size_t)L.Mp * 4);
     L.keysB = take((size_t)L.Mp * 4);
     L.valsB = take((size_t)L.Mp * 4);
-    // one fp32 partial per (vocabulary slice, K split): written once, summed by the finish
-    L.dhpart = take((size_t)std::min(L.n_chunks, kSlotSlices) * kMaxSplitDh * L.Mp * H * 4);
+    // fp32 dHidden partial slabs, one per K split (at most 2 Mp x H floats in
+    // all); every slice adds into them, the finish sums them
+    L.dhpart = take((size_t)2 * L.Mp * H * 4);
     L.spos = take((size_t)L.Mp * 4);
     L.sw = take((size_t)L.Mp * 4);
     L.ohcont = take((size_t)(L.Mp / 64) * H * 4);
@@ -613,9 +612,9 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
   GatherHTArgs gh{hidden, at<int>(ws, L.idx), hdr, H, L.Mp, L.ldt, HT};
   RUN("gather_ht", launch_gather_ht(gh, st));
 
-  // vocabulary slices: D, D^T for the slice; each slice writes its own
-  // dHidden partials (the finish adds them in a fixed order); each slice's dW
-  // rows are complete
+  // vocabulary slices: D, D^T for the slice; the first slice writes the
+  // dHidden partial slabs and later slices add to them in stream order (the
+  // finish sums the slabs in a fixed order); each slice's dW rows are complete
   float* dh_part = at<float>(ws, L.dhpart);
   // K steps of the first (widest) slice: the dHidden split count depends on it
   const int nkt_ref = (int)(align_up((size_t)std::min(V, L.chunk_tiles * gemm::BN), gemm::BN) / gemm::BK);
@@ -655,8 +654,8 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
     dh.max_split = kMaxSplitDh;
     dh.nkt_ref = nkt_ref;
     dh.hdr = hdr;
-    dh.part = dh_part + (size_t)(c % kSlotSlices) * kMaxSplitDh * L.Mp * H;
-    dh.accumulate = c >= kSlotSlices;
+    dh.part = dh_part;
+    dh.accumulate = c > 0;
     RUN("dhidden_gemm", launch_dh_gemm(dh, persistent_grid(), st));
 
     DwArgs dw;
@@ -687,7 +686,6 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
   df.hdr = hdr;
   df.H = H;
   df.Mp = L.Mp;
-  df.slices = std::min(L.n_chunks, kSlotSlices);
   df.max_split = kMaxSplitDh;
   df.nkt_ref = nkt_ref;
   df.grid = persistent_grid();
@@ -731,10 +729,6 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
   return DPO_OK;
 }
 }  // namespace
-
-extern "C" {
-
-}  // extern "C"
 
 namespace {
 int logits_forward(const void* logits, bool f32, const int32_t* targets, const uint8_t* mask, int rows,

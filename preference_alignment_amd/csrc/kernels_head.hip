@@ -21,8 +21,9 @@
 //   k_transpose_w    W^T (bf16) for the dHidden contraction
 //   k_gather_ht      Hc^T (bf16) for the dW contraction
 //   k_dprod_gemm     recompute Z tile; epilogue D = w exp(z - lse) -> bf16 D, D^T (softmax part)
-//   k_dh_gemm        dHidden partials = D . W over vocabulary halves (split K)
-//   k_dh_finish      dHidden rows = sum of partials - w W[target], scattered to their positions
+//   k_dh_gemm        dHidden partials = D . W, K split in parts; each part's fp32 slab
+//                    accumulates over the vocabulary slices
+//   k_dh_finish      dHidden rows = sum of the slabs - w W[target], scattered to their positions
 //   k_dw_gemm        dW_vocab = D^T . Hc (overwrite or accumulate)
 //   k_sort_targets   completion positions stably sorted by target id
 //   k_onehot_dw(+_join) dW_vocab[y] -= sum of w h over the positions whose target is y
@@ -550,19 +551,25 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dHidden = D . W  (R = D rows, C = W^T rows), K = the slice's vocabulary
-// split in dh_splits() parts, each written as an fp32 partial; k_dh_finish
-// adds them in a fixed order, applies the exact one-hot term and scatters rows
-// to their positions.
+// split in dh_splits() parts.  Part ks of every slice accumulates into fp32
+// slab ks (the first slice writes it, later ones add to it: the slices run in
+// stream order, so the order of the additions is fixed); k_dh_finish adds the
+// slabs in a fixed order, applies the exact one-hot term and scatters rows to
+// their positions.
 // ---------------------------------------------------------------------------
 // The dHidden contraction has few output tiles (positions x H), so K (the
 // slice's vocabulary) is split to fill the CUs: the split count minimises
-// rounds of tiles over the grid times K steps per tile (ties to fewer parts).
-// It depends on N_c, which only the device knows; the finish recomputes it.
-__device__ __forceinline__ int dh_splits(int n_c, int H, int nkt, int grid, int max_split) {
-  const long tiles = (long)cdiv(n_c, BM) * cdiv(H, BN);
+// rounds of tiles over the grid times K steps per tile (ties to fewer parts),
+// among the counts whose slabs (align(n_c, 256) x H floats each) fit in the
+// 2 Mp x H floats the workspace holds.  It depends on N_c, which only the
+// device knows; the finish recomputes it.
+__device__ __forceinline__ int dh_splits(int n_c, int H, int nkt, int grid, int max_split, int Mp) {
+  const int mt = cdiv(n_c, BM);
+  const long tiles = (long)mt * cdiv(H, BN);
+  const int cap = mt > 0 ? (2 * Mp) / (mt * BM) : max_split;
   int best = 1;
   long best_cost = -1;
-  for (int s = 1; s <= max_split && s <= max(nkt, 1); ++s) {
+  for (int s = 1; s <= max_split && s <= max(nkt, 1) && s <= cap; ++s) {
     const long cost = (tiles * s + grid - 1) / grid * cdiv(nkt, s);
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
@@ -570,6 +577,65 @@ __device__ __forceinline__ int dh_splits(int n_c, int H, int nkt, int grid, int 
     }
   }
   return best;
+}
+
+// slab ks of the dHidden partial sums: align(n_c, BM) rows of H floats each
+__device__ __forceinline__ size_t dh_slab(int n_c, int H) { return (size_t)cdiv(n_c, BM) * BM * H; }
+
+// The fp32 tile leaves through LDS in two halves of 128 rows (the pipeline
+// buffers are free after the main loop): the waves owning a half write their
+// accumulators into a 128 x 256 float table (16-column blocks XOR-swizzled by
+// row so the four row groups of a wave's write land in distinct banks), then
+// all threads move it as 16-byte vectors, one 1 KiB row per wave.  With
+// `accumulate`, the slab's current values of the half are loaded first (16
+// coalesced loads per thread in flight together) and the sums stored.
+__device__ __forceinline__ int dh_stage_col(int row, int col) { return col ^ (((row >> 2) & 3) << 4); }
+
+__device__ __forceinline__ void dh_store_tile(const Acc& acc, float* part, int m0, int n0, int n_c, int H,
+                                              int accumulate, char* smem, int tid, int lane, int wm, int wn) {
+  float* stage = (float*)smem;
+  constexpr int kIters = (BM / 2) * BN / 4 / NTHREADS;  // 16 float4 per thread per half
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < ACC_N; ++e) {
+          const int row = i * FRAG + 4 * (lane >> 4) + e;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            stage[row * BN + dh_stage_col(row, acc_col(wn, j, lane))] = acc.c[i][j][e];
+        }
+    }
+    __syncthreads();
+    float4 old[kIters];
+    if (accumulate) {
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int g = it * NTHREADS + tid;
+        const int row = g >> 6, c4 = g & 63;
+        const int m = m0 + h * (BM / 2) + row, col = n0 + c4 * 4;
+        old[it] = (m < n_c && col < H) ? *(const float4*)(part + (size_t)m * H + col)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int g = it * NTHREADS + tid;
+      const int row = g >> 6, c4 = g & 63;
+      const int m = m0 + h * (BM / 2) + row, col = n0 + c4 * 4;
+      float4 v = *(const float4*)(stage + row * BN + dh_stage_col(row, c4 * 4));
+      if (accumulate) {
+        v.x += old[it].x;
+        v.y += old[it].y;
+        v.z += old[it].z;
+        v.w += old[it].w;
+      }
+      if (m < n_c && col < H) *(float4*)(part + (size_t)m * H + col) = v;
+    }
+    __syncthreads();
+  }
 }
 
 __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
@@ -581,8 +647,9 @@ __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
   const int n_c = a.hdr->n_c;
   const int nNt = cdiv(a.H, BN);
   const int nkt = a.Vp / BK;
-  const int splitk = dh_splits(n_c, a.H, a.nkt_ref, gridDim.x, a.max_split);
+  const int splitk = dh_splits(n_c, a.H, a.nkt_ref, gridDim.x, a.max_split, a.Mp);
   const int nks = cdiv(nkt, splitk);
+  const size_t slab = dh_slab(n_c, a.H);
   Sched sc;
   sc.init(cdiv(n_c, BM), nNt * splitk, a.gm);
   for (int t = sc.begin; t < sc.end; t += sc.step) {
@@ -596,45 +663,32 @@ __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
     const RowOperand wop = row_operand(a.wt + (size_t)n0 * a.ldw, a.ldw, (long)a.H - n0, kb * BK, tid);
     Acc acc;
     mainloop(acc, dop, wop, nk, smem, wave, lane, wm, wn);
-    float* part = a.part + (size_t)ks * a.Mp * a.H;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int e = 0; e < ACC_N; ++e) {
-        const int m = m0 + acc_row(wm, i, e, lane);
-        if (m >= n_c) continue;
-        float* dst = part + (size_t)m * a.H;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + acc_col(wn, j, lane);
-          if (col < a.H) dst[col] = a.accumulate ? dst[col] + acc.c[i][j][e] : acc.c[i][j][e];
-        }
-      }
-    }
+    float* part = a.part + (size_t)ks * slab;
+    dh_store_tile(acc, part, m0, n0, n_c, a.H, a.accumulate, smem, opaque(tid), opaque(lane), wm, wn);
     __syncthreads();
   }
 }
 
-// one block per completion position: dH = sum of partials - w W[target]
+// one block per completion position: dH = sum of the slabs - w W[target]
 __global__ __launch_bounds__(256) void k_dh_finish(DhFinishArgs a) {
   const int m = blockIdx.x;
-  if (m >= a.hdr->n_c) return;
+  const int n_c = a.hdr->n_c;
+  if (m >= n_c) return;
   const int tg = a.tgt_c[m];
   const float wr = tg >= 0 ? a.weight[a.row_c[m]] : 0.f;
   const uint16_t* wrow = a.w + (size_t)(tg >= 0 ? tg : 0) * a.H;
   float* dst = a.d_hidden + (size_t)a.idx[m] * a.H;
-  const int splitk = dh_splits(a.hdr->n_c, a.H, a.nkt_ref, a.grid, a.max_split);
+  const int splitk = dh_splits(n_c, a.H, a.nkt_ref, a.grid, a.max_split, a.Mp);
+  const size_t slab = dh_slab(n_c, a.H);
   for (int c = threadIdx.x * 4; c < a.H; c += 256 * 4) {
-    // slice slot by slice slot, split by split
     float4 s = *(const float4*)(a.part + (size_t)m * a.H + c);
-    for (int q = 0; q < a.slices; ++q)
-      for (int ks = q == 0 ? 1 : 0; ks < splitk; ++ks) {
-        const float4 p = *(const float4*)(a.part + ((size_t)(q * a.max_split + ks) * a.Mp + m) * a.H + c);
-        s.x += p.x;
-        s.y += p.y;
-        s.z += p.z;
-        s.w += p.w;
-      }
+    for (int ks = 1; ks < splitk; ++ks) {
+      const float4 p = *(const float4*)(a.part + ks * slab + (size_t)m * a.H + c);
+      s.x += p.x;
+      s.y += p.y;
+      s.z += p.z;
+      s.w += p.w;
+    }
     const uint2 wv = *(const uint2*)(wrow + c);
     s.x = fmaf(-wr, bf16_lo(wv.x), s.x);
     s.y = fmaf(-wr, bf16_hi(wv.x), s.y);

@@ -127,11 +127,11 @@ struct DhArgs {
   const uint16_t* D;    // [Mp, Vp] the slice's D
   const uint16_t* wt;   // [H, ldw] W^T, offset to the slice's first vocabulary column
   int H, V, Vp, ldw, Mp, gm;
-  int max_split;  // partial slots of the slice; the kernel splits K into dh_splits(...) <= this parts
+  int max_split;  // the kernel splits K into dh_splits(...) <= this many parts
   int nkt_ref;    // K steps of the first slice: every slice and the finish choose the same split count
-  int accumulate;  // add into the partials (slices beyond the slot count)
+  int accumulate;  // 0: the first slice writes the slabs; 1: later slices add to them
   const WsHeader* hdr;
-  float* part;  // [max_split, Mp, H] fp32 partial sums
+  float* part;  // split slabs, each align(n_c, 256) x H fp32, 2 Mp x H floats in all
 };
 
 struct DhFinishArgs {
@@ -143,8 +143,7 @@ struct DhFinishArgs {
   const float* weight;  // [rows]
   const WsHeader* hdr;
   int H, Mp;
-  int slices;     // slice slots holding partials
-  int max_split;  // partial slots per slice slot
+  int max_split;
   int nkt_ref, grid;  // as for k_dh_gemm: the same split count
   float* d_hidden;  // [rows*T, H]
 };
