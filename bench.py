@@ -28,7 +28,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published figure)
+# the same peak from the unit counts: 256 CUs x 2.4 GHz x 4,096 bf16 flop per clock per CU
+PEAK_BF16_TFLOPS_UNITS = 256 * 2.4e9 * 4096 / 1e12  # 2,516.6
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 METRICS = {
@@ -110,11 +112,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=None,
-                   help="completion positions per sampled row for the CPU baseline (0 = all); "
-                        "default 1024 for the fused head, all for given logits")
+    p.add_argument("--cpu-sample-tokens", type=int, default=0,
+                   help="completion positions per sampled row for the CPU baseline (0 = all: whole pairs)")
     p.add_argument("--cpu-sample-pairs", type=int, default=None,
-                   help="pairs in the CPU baseline sample; default 1 for the fused head, 2 for given logits")
+                   help="whole pairs in the CPU baseline sample; default 1 for the fused head's fwd+bwd, "
+                        "2 for reference scoring (forward only) and for given logits")
     p.add_argument("--no-kernel-timing", action="store_true")
     p.add_argument("--all-kernel-timing", action="store_true",
                    help="bracket every kernel with events inside the timed region (default: only the dominant "
@@ -420,16 +422,20 @@ def main():
             D.dpo_profile_select(dom)
         D.dpo_profile_enable(True)
     stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event between consecutive steps gives each step's time (for the
+    # median) while the first and last bracket the whole timed region
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     torch.cuda.synchronize()
     t_host = time.perf_counter()
-    e0.record(stream)
-    for _ in range(a.steps):
+    ev[0].record(stream)
+    for i in range(a.steps):
         runner.step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
-    ms = e0.elapsed_time(e1)
+    ms = ev[0].elapsed_time(ev[-1])
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps))
+    ms_median = float(np.median(step_ms))
     timed_kernels = {}
     if not a.no_kernel_timing:
         timed_kernels = D.dpo_profile_read()
@@ -460,6 +466,7 @@ def main():
                 "algorithmic_bytes_per_launch": per_kernel_bytes[dom]}
         step_bytes = n_c * V * eb * 2 + E * eb
         extra = {"step_hbm_frac": step_bytes / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS,
+                 "step_hbm_frac_median": step_bytes / (ms_median / 1e3) / 1e9 / PEAK_HBM_GBS,
                  "kernels_ms_per_step": {k: round(v[0] / kernels_steps, 4) for k, v in kernels.items()}}
     else:
         gemms = candidates
@@ -472,27 +479,39 @@ def main():
         ach = flops / (avg / 1e3) / 1e12 if avg else None
         roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS if ach else None,
+                "frac_of_unit_count_peak": ach / PEAK_BF16_TFLOPS_UNITS if ach else None,
                 "traffic": measured_traffic(dom, label), "avg_ms": avg,
                 "algorithmic_flops_per_launch": flops}
+        # the step's contractions: 4 x 2 H V flops per completion token for the
+        # fused step (the recomputed forward included), 3 x 2 H V useful
         step_flops = flops_step * len(gemms)
-        extra = {"step_mfma_frac": step_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-                 "step_useful_mfma_frac": (flops_step * (1 if a.workload == 3 else 3)) / (ms_step / 1e3) / 1e12
-                 / PEAK_BF16_TFLOPS,
+        useful = flops_step * (1 if a.workload == 3 else 3)
+        tf = 1.0 / (ms_step / 1e3) / 1e12
+        tf_med = 1.0 / (ms_median / 1e3) / 1e12
+        extra = {"step_mfma_frac": step_flops * tf / PEAK_BF16_TFLOPS,
+                 "step_useful_mfma_frac": useful * tf / PEAK_BF16_TFLOPS,
+                 "step_mfma_frac_of_unit_count_peak": step_flops * tf / PEAK_BF16_TFLOPS_UNITS,
+                 "step_useful_mfma_frac_of_unit_count_peak": useful * tf / PEAK_BF16_TFLOPS_UNITS,
+                 "step_mfma_frac_median": step_flops * tf_med / PEAK_BF16_TFLOPS,
+                 "peaks_tflops": {"published": PEAK_BF16_TFLOPS, "unit_count": round(PEAK_BF16_TFLOPS_UNITS, 1)},
                  "kernels_ms_per_step": {k: round(v[0] / kernels_steps, 4) for k, v in kernels.items()}}
 
     cpu = None
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         given_logits = x.logits is not None
-        tokens = a.cpu_sample_tokens if a.cpu_sample_tokens is not None else (0 if given_logits else 1024)
-        pairs = a.cpu_sample_pairs if a.cpu_sample_pairs is not None else (min(2, x.num_pairs) if given_logits else 1)
-        cpu = cpu_baseline(x, a.workload, tokens, row, runner.Vs if row == "vocab-shard" else None, pairs)
+        pairs = a.cpu_sample_pairs if a.cpu_sample_pairs is not None else (
+            min(2, x.num_pairs) if (given_logits or a.workload == 3) else 1)
+        cpu = cpu_baseline(x, a.workload, a.cpu_sample_tokens, row, runner.Vs if row == "vocab-shard" else None,
+                           pairs)
 
     metric = METRICS[a.workload] if row == "main" else ROW_METRICS[row].format(
         H=H, V=V, Vs=getattr(runner, "Vs", V))
     line = {
         "metric": metric, "value": value, "unit": "completion tokens/s", "n_gpus": 1,
-        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_step, "ms_per_step_median": ms_median,
+        "ms_per_step_min": step_ms[0], "ms_per_step_max": step_ms[-1],
+        "value_median": n_c / (ms_median / 1e3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32" if row == "f32-logits" else "bf16",
         "data": "synthetic",
         "config": {"workload": f"workload{a.workload}: {W.WORKLOADS[a.workload][0]}"
