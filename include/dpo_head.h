@@ -61,7 +61,8 @@ enum {
   DPO_ERR_WORKSPACE = -6,    /* workspace smaller than dpo_workspace_bytes() */
   DPO_ERR_TARGET_RANGE = -7, /* device-detected target id outside [0, V) */
   DPO_ERR_HIP = -8,          /* a HIP runtime call failed */
-  DPO_ERR_ALPHA = -9         /* sft_alpha is not finite and >= 0 */
+  DPO_ERR_ALPHA = -9,        /* sft_alpha is not finite and >= 0 */
+  DPO_ERR_SCRATCH = -10      /* sizes beyond the no-allocation entry point's static scratch */
 };
 
 /* Pair layouts of the concatenated batch.
@@ -294,6 +295,25 @@ int dpo_seq_logps_metrics(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
                           void* workspace, size_t workspace_bytes, void* stream);
 int dpo_logits_mean(const double* logit_sum, const int32_t* n_tokens, int num_pairs, int V,
                     int layout, float* means, void* stream);
+
+/* dpo_logits_seq_logps without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  It allocates nothing and calls no allocating
+ * routine: its scratch (a 256-byte status header, fp64 log p and a target
+ * flag per position) is a static device array of 12 MiB + 256 bytes that each
+ * GPU the library runs on holds until the process ends.
+ *   Same inputs and outputs as dpo_logits_seq_logps, without workspace, plus
+ *   status [1] int32 (device): DPO_OK, or DPO_ERR_TARGET_RANGE if a target at
+ *   a completion position lies outside [0, V); written on `stream` at the end
+ *   of the call (dpo_device_status does not apply: there is no workspace).
+ * Limit: rows * T <= 2^20 positions, else DPO_ERR_SCRATCH before any launch.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents: calls that overlap in time on one GPU (different streams
+ * without ordering, or different host threads) race and give wrong results.
+ * Calls ordered on one stream are safe. */
+int dpo_logits_seq_logps_noalloc(const dpo_bf16* logits, const int32_t* targets, const uint8_t* mask,
+                                 int rows, int T, int V, float* logp_sum, double* logp_sum64, float* lse,
+                                 int32_t* n_tokens, int32_t* status, void* stream);
 
 /* Waits for `stream`, then returns DPO_ERR_TARGET_RANGE if the most recent
  * call that used `workspace` met a target id outside [0, V) at a completion

@@ -37,6 +37,38 @@ constexpr int kTransPad = 64;  // elements
 constexpr int kStreamBwdBlocksPerCU = 32;
 
 // ---------------------------------------------------------------------------
+// static scratch of the no-allocation entry point
+// ---------------------------------------------------------------------------
+// dpo_logits_seq_logps_noalloc keeps its scratch (status header, per-position
+// fp64 log p and target flags) in this file-scope device array instead of a
+// caller workspace, for callers that cannot allocate.  Each GPU the library
+// runs on holds its own copy until the process ends; host code reaches it only
+// through the address hipGetSymbolAddress returns for the current device.
+constexpr long kNoAllocMaxPositions = 1L << 20;  // rows * T
+constexpr size_t kScratchLogpOff = 256;
+constexpr size_t kScratchBadOff = kScratchLogpOff + (size_t)kNoAllocMaxPositions * 8;
+constexpr size_t kScratchBytes = kScratchBadOff + (size_t)kNoAllocMaxPositions * 4;  // 12 MiB + 256 B
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+char* g_scratch_addr[kMaxDevices] = {};
+
+// The scratch's device address on the current device, looked up once per device.
+int noalloc_scratch(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DPO_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DPO_ERR_HIP;
+    g_scratch_addr[dev] = (char*)p;
+  }
+  *out = g_scratch_addr[dev];
+  return DPO_OK;
+}
+
+// ---------------------------------------------------------------------------
 // workspace layout
 // ---------------------------------------------------------------------------
 struct Layout {
@@ -731,27 +763,18 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
 }  // namespace
 
 namespace {
-int logits_forward(const void* logits, bool f32, const int32_t* targets, const uint8_t* mask, int rows,
-                   int T, int V, float* logp_sum, double* logp_sum64, float* lse, int32_t* n_tokens,
-                   void* workspace, size_t workspace_bytes, void* stream) {
-  if (!logits || !logp_sum) return DPO_ERR_NULL;
-  int rc = check_common(targets, mask, rows, T, 0, V, false, DPO_OP_LOGITS_SEQ_LOGPS, workspace_bytes,
-                        workspace);
-  if (rc) return rc;
-  if (!aligned16(logits) || !aligned16(logp_sum) || (logp_sum64 && !aligned16(logp_sum64)) ||
-      (lse && !aligned16(lse)))
-    return DPO_ERR_ALIGN;
-  hipStream_t st = (hipStream_t)stream;
-  const Layout L = make_layout(DPO_OP_LOGITS_SEQ_LOGPS, rows, T, 0, V);
-  void* ws = workspace;
+// the two launches of the logits forward, on explicit scratch pointers
+int enqueue_logits_forward(const void* logits, bool f32, const int32_t* targets, const uint8_t* mask, int rows,
+                           int T, int V, float* logp_sum, double* logp_sum64, float* lse, int32_t* n_tokens,
+                           WsHeader* hdr, double* logp64, int* bad, hipStream_t st) {
   StreamFwdArgs f;
   f.logits = logits;
   f.targets = targets;
   f.mask = mask;
   f.V = V;
-  f.hdr = at<WsHeader>(ws, L.hdr);
-  f.logp64 = at<double>(ws, L.logp64);
-  f.bad = at<int>(ws, L.idx);
+  f.hdr = hdr;
+  f.logp64 = logp64;
+  f.bad = bad;
   f.lse_out = lse;
   if (f32)
     RUN("stream_fwd_f32", launch_stream_fwd_f32(f, (long)rows * T, st));
@@ -769,6 +792,23 @@ int logits_forward(const void* logits, bool f32, const int32_t* targets, const u
   r.n_tokens = n_tokens;
   RUN("row_sums", launch_stream_row_sums(r, st));
   return DPO_OK;
+}
+
+int logits_forward(const void* logits, bool f32, const int32_t* targets, const uint8_t* mask, int rows,
+                   int T, int V, float* logp_sum, double* logp_sum64, float* lse, int32_t* n_tokens,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !logp_sum) return DPO_ERR_NULL;
+  int rc = check_common(targets, mask, rows, T, 0, V, false, DPO_OP_LOGITS_SEQ_LOGPS, workspace_bytes,
+                        workspace);
+  if (rc) return rc;
+  if (!aligned16(logits) || !aligned16(logp_sum) || (logp_sum64 && !aligned16(logp_sum64)) ||
+      (lse && !aligned16(lse)))
+    return DPO_ERR_ALIGN;
+  const Layout L = make_layout(DPO_OP_LOGITS_SEQ_LOGPS, rows, T, 0, V);
+  void* ws = workspace;
+  return enqueue_logits_forward(logits, f32, targets, mask, rows, T, V, logp_sum, logp_sum64, lse, n_tokens,
+                                at<WsHeader>(ws, L.hdr), at<double>(ws, L.logp64), at<int>(ws, L.idx),
+                                (hipStream_t)stream);
 }
 
 int logits_backward(const void* logits, bool f32, const int32_t* targets, const uint8_t* mask, int rows,
@@ -831,6 +871,27 @@ int dpo_logits_f32_backward(const float* logits, const int32_t* targets, const u
                          workspace_bytes, stream);
 }
 
+int dpo_logits_seq_logps_noalloc(const dpo_bf16* logits, const int32_t* targets, const uint8_t* mask,
+                                 int rows, int T, int V, float* logp_sum, double* logp_sum64, float* lse,
+                                 int32_t* n_tokens, int32_t* status, void* stream) {
+  if (!logits || !targets || !mask || !logp_sum || !status) return DPO_ERR_NULL;
+  if (!shape_ok(rows, T, 0, V, false)) return DPO_ERR_SHAPE;
+  if ((long long)rows * T > kNoAllocMaxPositions) return DPO_ERR_SCRATCH;
+  if (!aligned16(logits) || !aligned16(logp_sum) || (logp_sum64 && !aligned16(logp_sum64)) ||
+      (lse && !aligned16(lse)))
+    return DPO_ERR_ALIGN;
+  char* base = nullptr;
+  int rc = noalloc_scratch(&base);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  WsHeader* hdr = (WsHeader*)base;
+  rc = enqueue_logits_forward(logits, false, targets, mask, rows, T, V, logp_sum, logp_sum64, lse, n_tokens, hdr,
+                              (double*)(base + kScratchLogpOff), (int*)(base + kScratchBadOff), st);
+  if (rc) return rc;
+  RUN("write_status", launch_write_status(hdr, DPO_ERR_TARGET_RANGE, status, st));
+  return DPO_OK;
+}
+
 int dpo_device_status(void* workspace, void* stream) {
   if (!workspace) return DPO_ERR_NULL;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DPO_ERR_HIP;
@@ -852,6 +913,7 @@ const char* dpo_strerror(int status) {
       return "a target id at a completion position is outside [0, V) (or no vocabulary shard holds it)";
     case DPO_ERR_HIP: return "a HIP runtime call failed";
     case DPO_ERR_ALPHA: return "sft_alpha must be finite and >= 0";
+    case DPO_ERR_SCRATCH: return "rows * T exceeds the 2^20 positions of the no-allocation scratch";
     default: return "unknown status";
   }
 }

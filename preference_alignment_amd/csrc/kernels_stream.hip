@@ -254,6 +254,12 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_bwd(StreamBwdArgs a, 
 
 __global__ void k_reset_status(WsHeader* hdr) { hdr->status = 0; }
 
+// the call's status for a caller without a workspace: `code` if a target was
+// out of range, else 0
+__global__ void k_write_status(const WsHeader* hdr, int code, int32_t* out) {
+  out[0] = (hdr->status & kStatusTargetRange) ? code : 0;
+}
+
 // ---------------------------------------------------------------------------
 // sigmoid DPO loss, fp64
 // ---------------------------------------------------------------------------
@@ -415,6 +421,11 @@ hipError_t launch_stream_row_sums(const StreamRowSumArgs& a, hipStream_t s) {
 
 hipError_t launch_logits_mean(const LogitsMeanArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_logits_mean, dim3(1), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_status(const WsHeader* hdr, int code, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_write_status, dim3(1), dim3(1), 0, s, hdr, code, out);
   return hipGetLastError();
 }
 

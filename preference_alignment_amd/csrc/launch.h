@@ -259,6 +259,7 @@ hipError_t launch_stream_fwd(const StreamFwdArgs& a, long positions, hipStream_t
 hipError_t launch_stream_row_sums(const StreamRowSumArgs& a, hipStream_t s);
 hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, int grid, hipStream_t s);
 hipError_t launch_reset_status(WsHeader* hdr, hipStream_t s);
+hipError_t launch_write_status(const WsHeader* hdr, int code, int32_t* out, hipStream_t s);
 hipError_t launch_loss(const LossArgs& a, hipStream_t s);
 hipError_t launch_shard_partials(const ShardPartialArgs& a, int Mp, hipStream_t s);
 hipError_t launch_shard_combine(const ShardCombineArgs& a, int Mp, hipStream_t s);

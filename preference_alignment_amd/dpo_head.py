@@ -25,6 +25,7 @@ DPO_ERR_WORKSPACE = -6
 DPO_ERR_TARGET_RANGE = -7
 DPO_ERR_HIP = -8
 DPO_ERR_ALPHA = -9
+DPO_ERR_SCRATCH = -10
 
 DPO_PAIRS_ADJACENT = 0
 DPO_PAIRS_HALVES = 1
@@ -63,6 +64,7 @@ _SIGS = {
                                      _P]),
     "dpo_seq_logps_metrics": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dpo_logits_mean": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "dpo_logits_seq_logps_noalloc": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "dpo_device_status": (_I, [_P, _P]),
     "dpo_strerror": (ctypes.c_char_p, [_I]),
     "dpo_profile_enable": (_I, [_I]),
@@ -115,7 +117,7 @@ def _check(status: int) -> None:
         return
     msg = lib().dpo_strerror(status).decode()
     if status in (DPO_ERR_NULL, DPO_ERR_SHAPE, DPO_ERR_ALIGN, DPO_ERR_BETA, DPO_ERR_LAYOUT,
-                  DPO_ERR_WORKSPACE, DPO_ERR_ALPHA):
+                  DPO_ERR_WORKSPACE, DPO_ERR_ALPHA, DPO_ERR_SCRATCH):
         raise ValueError(f"{msg} (status {status})")
     raise DpoError(status, msg)
 
@@ -279,6 +281,31 @@ def dpo_logits_seq_logps(logits, targets, mask, logp_sum, logp_sum64=None, lse=N
         _check(lib().dpo_logits_seq_logps(_d.p(logits), _d.p(targets), _d.p(mask), rows, T, V, _d.p(logp_sum),
                                           _d.p(logp_sum64), _d.p(lse), _d.p(n_tokens), _d.p(workspace),
                                           workspace.numel(), _stream(stream, logits)))
+
+
+def dpo_logits_seq_logps_noalloc(logits, targets, mask, logp_sum, status, logp_sum64=None, lse=None,
+                                 n_tokens=None, stream=None) -> None:
+    """The logits forward on the library's static scratch (no workspace, no
+    allocation); ``status`` is a one-element int32 device tensor that receives
+    DPO_OK or DPO_ERR_TARGET_RANGE on the stream."""
+    import torch
+    rows, T, V = logits.shape
+    _need(logits, torch.bfloat16, "logits")
+    _need(targets, torch.int32, "targets", (rows, T))
+    _need(mask, torch.uint8, "mask", (rows, T))
+    _need(logp_sum, torch.float32, "logp_sum", (rows,))
+    _need(status, torch.int32, "status", (1,))
+    if logp_sum64 is not None:
+        _need(logp_sum64, torch.float64, "logp_sum64", (rows,))
+    if lse is not None:
+        _need(lse, torch.float32, "lse", (rows, T))
+    if n_tokens is not None:
+        _need(n_tokens, torch.int32, "n_tokens", (rows,))
+    _d = _Dev(logits)
+    with torch.cuda.device(_d.dev):
+        _check(lib().dpo_logits_seq_logps_noalloc(_d.p(logits), _d.p(targets), _d.p(mask), rows, T, V,
+                                                  _d.p(logp_sum), _d.p(logp_sum64), _d.p(lse), _d.p(n_tokens),
+                                                  _d.p(status), _stream(stream, logits)))
 
 
 def dpo_logits_backward(logits, targets, mask, lse, weight, d_logits, workspace=None, stream=None) -> None:
