@@ -28,9 +28,9 @@ constexpr int kGroupBwd = 4;
 // fp32 slabs take at most 2 Mp x H floats (the device caps the count to fit),
 // and every vocabulary slice adds into the same slabs.
 constexpr int kMaxSplitDh = 4;
-// The backward holds the bf16 softmax part of dlogits (D and D^T) only for one
-// slice of the vocabulary at a time: each of D and D^T stays under this many
-// bytes (balanced slices of whole 256-wide tiles).
+// The backward holds the bf16 softmax part of dlogits (D) only for one slice
+// of the vocabulary at a time: D stays under this many bytes (balanced slices
+// of whole 256-wide tiles).
 constexpr size_t kChunkBytes = size_t(1) << 30;
 constexpr int kTransPad = 64;  // elements
 // workgroups per CU of the chunked streaming backward
@@ -77,10 +77,10 @@ struct Layout {
   int nVt = 0;  // vocabulary tiles of the forward contraction
   int chunk_tiles = 0;  // vocabulary tiles per backward slice
   int n_chunks = 0;
-  int ldt = 0;  // row stride (elements) of D^T and Hc^T: positions plus a pad
+  int ldt = 0;  // row stride (elements) of Hc^T: positions plus a pad
   size_t hdr = 0, idx = 0, tgt = 0, rowc = 0, rowoff = 0;
   size_t part = 0, tlogit = 0, lse64 = 0, logp64 = 0, partz = 0, zsum64 = 0;
-  size_t D = 0, DT = 0, WT = 0, HT = 0;
+  size_t D = 0, HT = 0;
   size_t keysA = 0, valsA = 0, keysB = 0, valsB = 0, dhpart = 0, spos = 0, sw = 0, ohcont = 0, ohhead = 0;
   size_t total = 0;
 };
@@ -143,13 +143,11 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     L.n_chunks = cdiv(L.nVt, max_tiles);
     L.chunk_tiles = cdiv(L.nVt, L.n_chunks);
     const size_t Vcp = (size_t)L.chunk_tiles * gemm::BN;
-    // D^T and Hc^T rows are positions long; a pad of 128 bytes keeps their
-    // stride off a power of two (2^15 bytes at 16,384 positions), where all
-    // rows of a tile would fall on the same HBM channels
+    // Hc^T rows are positions long; a pad of 128 bytes keeps their stride off
+    // a power of two (2^15 bytes at 16,384 positions), where all rows of a
+    // tile would fall on the same HBM channels
     L.ldt = L.Mp + kTransPad;
     L.D = take((size_t)L.Mp * Vcp * 2);
-    L.DT = take(Vcp * L.ldt * 2);
-    L.WT = take((size_t)H * L.Vp * 2);
     L.HT = take((size_t)H * L.ldt * 2);
     L.keysA = take((size_t)L.Mp * 4);
     L.valsA = take((size_t)L.Mp * 4);
@@ -165,6 +163,15 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
   }
   L.total = o;
   return L;
+}
+
+// The backward's contractions address one vocabulary slice of D and of W
+// with 32-bit byte offsets: both must stay under 4 GiB.
+bool backward_addressable(int op, int rows, int T, int H, int V) {
+  if (op != DPO_OP_HEAD_BACKWARD) return true;
+  const Layout L = make_layout(op, rows, T, H, V);
+  const size_t vc = (size_t)L.chunk_tiles * gemm::BN;
+  return (size_t)L.Mp * vc * 2 < (size_t(1) << 32) && vc * (size_t)H * 2 < (size_t(1) << 32);
 }
 
 template <typename T>
@@ -276,7 +283,7 @@ hipError_t timed(const char* name, hipStream_t s, F f) {
 int check_common(const void* targets, const void* mask, int rows, int T, int H, int V, bool need_h,
                  int op, size_t ws_bytes, const void* ws) {
   if (!targets || !mask || !ws) return DPO_ERR_NULL;
-  if (!shape_ok(rows, T, H, V, need_h)) return DPO_ERR_SHAPE;
+  if (!shape_ok(rows, T, H, V, need_h) || !backward_addressable(op, rows, T, H, V)) return DPO_ERR_SHAPE;
   if (!aligned16(ws)) return DPO_ERR_ALIGN;
   if (ws_bytes < make_layout(op, rows, T, H, V).total) return DPO_ERR_WORKSPACE;
   return DPO_OK;
@@ -410,7 +417,7 @@ extern "C" {
 size_t dpo_workspace_bytes(int op, int rows, int T, int H, int V) {
   if (!op_known(op)) return 0;
   const bool need_h = op_needs_h(op);
-  if (!shape_ok(rows, T, H, V, need_h)) return 0;
+  if (!shape_ok(rows, T, H, V, need_h) || !backward_addressable(op, rows, T, H, V)) return 0;
   return make_layout(op, rows, T, need_h ? H : 0, V).total;
 }
 
@@ -635,16 +642,12 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
   if (rc) return rc;
   WsHeader* hdr = at<WsHeader>(ws, L.hdr);
   uint16_t* D = at<uint16_t>(ws, L.D);
-  uint16_t* DT = at<uint16_t>(ws, L.DT);
-  uint16_t* WT = at<uint16_t>(ws, L.WT);
   uint16_t* HT = at<uint16_t>(ws, L.HT);
 
-  TransposeWArgs tw{w_vocab, V, H, L.Vp, WT};
-  RUN("transpose_w", launch_transpose_w(tw, st));
   GatherHTArgs gh{hidden, at<int>(ws, L.idx), hdr, H, L.Mp, L.ldt, HT};
   RUN("gather_ht", launch_gather_ht(gh, st));
 
-  // vocabulary slices: D, D^T for the slice; the first slice writes the
+  // vocabulary slices: D for the slice; the first slice writes the
   // dHidden partial slabs and later slices add to them in stream order (the
   // finish sums the slabs in a fixed order); each slice's dW rows are complete
   float* dh_part = at<float>(ws, L.dhpart);
@@ -670,17 +673,14 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
     dp.lse = lse;
     dp.weight = weight;
     dp.D = D;
-    dp.DT = DT;
-    dp.ldt = L.ldt;
     RUN("dlogits_gemm", launch_dprod_gemm(dp, persistent_grid(), st));
 
     DhArgs dh;
     dh.D = D;
-    dh.wt = WT + v0;
+    dh.w = w_vocab + (size_t)v0 * H;
     dh.H = H;
     dh.V = Vc;
     dh.Vp = Vcp;
-    dh.ldw = L.Vp;
     dh.Mp = L.Mp;
     dh.gm = kGroupBwd;
     dh.max_split = kMaxSplitDh;
@@ -691,7 +691,7 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
     RUN("dhidden_gemm", launch_dh_gemm(dh, persistent_grid(), st));
 
     DwArgs dw;
-    dw.DT = DT;
+    dw.D = D;
     dw.ht = HT;
     dw.V = Vc;
     dw.H = H;

@@ -59,6 +59,18 @@ constexpr int NUM_XCD = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// The two pipeline stage buffers are distinct LDS objects.  The main loop is
+// unrolled over the pair, so every access names its buffer statically, and
+// the compiler can tell the direct-to-LDS loads into one buffer from reads
+// of the other: it then never waits for a stage's loads before a read of the
+// other stage (it did before transposing reads when both buffers were
+// offsets into one array).  The epilogues reuse the pair as staging space.
+static __shared__ __attribute__((aligned(16))) char g_stage0[STAGE_BYTES];
+static __shared__ __attribute__((aligned(16))) char g_stage1[STAGE_BYTES];
+#define DPO_STG(b_) ((b_) ? g_stage1 : g_stage0)
+// LDS byte address of a stage buffer (a constant once the kernel is laid out)
+#define DPO_STG_LDS(b_) ((unsigned)(size_t)(lds_ptr_t)DPO_STG(b_))
+
 struct Acc {
   floatx4 c[FM][FN];
 };
@@ -71,12 +83,40 @@ struct Acc {
 // descriptor, a 32-bit byte offset per lane and loaded row (fixed for the
 // tile), and the K step in the scalar offset.  Offsets at or beyond the
 // descriptor's size read as zero, which is how ragged tiles are padded.
+// Buffer resource of an operand (raw buffer, no stride): base address, its
+// size in bytes (reads at or past it return zero) and the format flags.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
 struct RowOperand {
-  __amdgpu_buffer_rsrc_t rsrc;
+  i32x4_t rsrc;
   unsigned voff[LOADS_PER_THREAD];  // byte offset of (row, lchunk * 8) at K = 0
 };
 
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit dwords
+
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, size_t bytes) {
+  const unsigned long long b = (unsigned long long)(size_t)base;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)min(bytes, (size_t)0xFFFFFFFFu));
+  r[3] = kBufferFlags;
+  return r;
+}
+
+// One 16-byte-per-lane direct-to-LDS load: lane L's 16 bytes land at
+// lds_wave + 16 L.  It is issued through inline assembly so that the compiler
+// does not track it: otherwise it waits for a stage's loads before reads of
+// the other stage whose aliasing it cannot rule out (it did before every
+// transposing read), while the loop's own stage barrier already waits for
+// them (vmcnt(0)) before any read of that stage.  The load writes no
+// register; its LDS destination is read only after that barrier.
+__device__ __forceinline__ void dma16(const i32x4_t& rsrc, unsigned lds_wave, unsigned voff, unsigned soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_wave), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
 
 // Operand whose tile rows are consecutive rows of a row-major matrix:
 // `base` = first row of the tile, `ld` = elements per row, `rows_left` = rows
@@ -85,8 +125,7 @@ __device__ __forceinline__ RowOperand row_operand(const uint16_t* base, size_t l
                                                   int tid) {
   RowOperand op;
   const size_t bytes = (size_t)max(rows_left, 0L) * ld * 2;
-  op.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
-                                              (int)min(bytes, (size_t)0xFFFFFFFFu), kBufferFlags);
+  op.rsrc = buffer_rsrc(base, bytes);
   const int lchunk = (tid & 7) ^ ((tid >> 4) & 7);
 #pragma unroll
   for (int it = 0; it < LOADS_PER_THREAD; ++it)
@@ -96,15 +135,52 @@ __device__ __forceinline__ RowOperand row_operand(const uint16_t* base, size_t l
 __device__ __forceinline__ int row_lchunk(int tid) { return (tid & 7) ^ ((tid >> 4) & 7); }
 __device__ __forceinline__ int row_loader_row(int it, int tid) { return it * LOADER_ROW_STRIDE + (tid >> 3); }
 
-__device__ __forceinline__ void load_stage(const RowOperand& op, int kstep, char* lds_tile, int wave) {
+__device__ __forceinline__ void load_stage(const RowOperand& op, int kstep, unsigned lds_tile, int wave) {
   const unsigned soff = __builtin_amdgcn_readfirstlane((unsigned)kstep * BK * 2);
 #pragma unroll
-  for (int it = 0; it < LOADS_PER_THREAD; ++it) {
-    lds_ptr_t dst = (lds_ptr_t)(lds_tile + (it * NTHREADS + wave * 64) * 16);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, dst, 16, op.voff[it], soff, 0, 0);
-  }
+  for (int it = 0; it < LOADS_PER_THREAD; ++it) dma16(op.rsrc, lds_tile + (it * NTHREADS + wave * 64) * 16, op.voff[it], soff);
 }
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// K-MAJOR operands are contiguous along the MFMA dimension (rows of memory =
+// K): a tile is 64 K rows x 512 bytes (256 values).  The 16-byte chunk c of K
+// row k sits at chunk c ^ kswz(k).  Each 16-lane group of a transposing
+// fragment read touches 4 K rows x 2 chunks, and the two groups of a
+// half-wave rows 8 apart; kswz gives those 8 rows 8 distinct even XOR values
+// below 16, so the 16 chunks a half-wave reads fall in distinct banks.
+__device__ __forceinline__ int kswz(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+
+// Loader of a K-major operand: `base` = element (K row 0, MN column 0) of
+// the tile, `ld` = elements per K row, `k_rows` = K rows that exist from base
+// on (rows past them read as zero through the descriptor's size).  The K step
+// is added to the per-lane offset (not the scalar one) so that every access
+// stays inside the descriptor's range check.
+struct KOperand {
+  i32x4_t rsrc;
+  unsigned voff[LOADS_PER_THREAD];  // byte offset of (K row, chunk) at K step 0
+  unsigned step;                    // bytes per K step of BK rows
+};
+
+__device__ __forceinline__ KOperand kmajor_operand(const uint16_t* base, size_t ld, long k_rows, int tid) {
+  KOperand op;
+  const size_t bytes = (size_t)max(k_rows, 0L) * ld * 2;
+  op.rsrc = buffer_rsrc(base, bytes);
+#pragma unroll
+  for (int it = 0; it < LOADS_PER_THREAD; ++it) {
+    const int k = it * (NTHREADS / 32) + (tid >> 5);
+    const int c = (tid & 31) ^ kswz(k);
+    op.voff[it] = (unsigned)(((size_t)k * ld + c * 8) * 2);
+  }
+  op.step = (unsigned)((size_t)BK * ld * 2);
+  return op;
+}
+
+__device__ __forceinline__ void load_stage(const KOperand& op, int kstep, unsigned lds_tile, int wave) {
+  const unsigned koff = (unsigned)kstep * op.step;
+#pragma unroll
+  for (int it = 0; it < LOADS_PER_THREAD; ++it)
+    dma16(op.rsrc, lds_tile + (it * NTHREADS + wave * 64) * 16, op.voff[it] + koff, 0);
+}
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr;
@@ -126,6 +202,44 @@ struct RowFrag {
   }
 };
 
+// Fragment reader of a K-major tile through ds_read_b64_tr_b16 (gfx950).  In
+// a 16-lane group the transposing read hands lane i element (i & 3) of the
+// 8-byte piece that lane 4 k + (i >> 2) addresses, for k = 0..3.  Lane L of
+// group g therefore addresses K row 8 g + (L >> 2) (+ 4 for the second
+// read), MFMA columns base + 16 f + 4 (L & 3) .. +3, and receives the K
+// values 8 g + 0..3 (then + 4..7) of column base + 16 f + (L & 15): the MFMA
+// operand layout.  A fragment's chunk is fragment 0's XOR 2 f (base is a
+// multiple of 64 and the swizzle only moves chunks within 16-chunk blocks),
+// so one offset per lane serves every fragment.
+struct TrFrag {
+  int off;  // byte offset of fragment 0's first read at step 0
+  __device__ __forceinline__ void init(int base, int lane) {
+    const int g = lane >> 4, L = lane & 15;
+    const int k = 8 * g + (L >> 2);
+    const int mn = base + 4 * (L & 3);
+    off = k * 512 + (((mn >> 3) ^ kswz(k)) << 4) + ((mn & 7) << 1);
+  }
+  __device__ __forceinline__ bf16x8_t read(const char* tile, int f, int s) const {
+    const char* p = tile + (off ^ (f << 5)) + s * (32 * 512);
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p);
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p + 4 * 512));
+    const short __attribute__((ext_vector_type(8))) v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+};
+
+// fragment reader and LDS reads per fragment of each operand kind
+template <typename Op>
+struct FragOf {
+  typedef RowFrag type;
+  static constexpr int reads = 1;
+};
+template <>
+struct FragOf<KOperand> {
+  typedef TrFrag type;
+  static constexpr int reads = 2;
+};
+
 // The K loop over nk steps of BK.  nk may be 0 (accumulators stay zero).  The
 // R operand supplies the MFMA rows (wave (wm, wn) owns rows wm*128 .. +128),
 // the C operand the MFMA columns (columns wn*64 .. +64).
@@ -140,10 +254,11 @@ struct RowFrag {
 // this stage's buffer); the loads two stages ahead into that buffer; rows
 // 1..7 of step 1, reading the next stage's step 0 into slot 0.  On the last
 // stage those reads fetch unused values from the idle buffer, which keeps
-// the loop free of branches inside the MFMA stream.
+// the loop free of branches inside the MFMA stream.  The loop body is
+// written twice, once per buffer of the pair.
 template <typename ROp, typename COp>
-__device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& cop, int nk, char* smem, int wave,
-                                         int lane, int wm, int wn) {
+__device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& cop, int nk, int wave, int lane,
+                                         int wm, int wn) {
   static_assert(FN <= FM, "B fragments are read behind the first FN rows");
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -153,12 +268,14 @@ __device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& co
       for (int e = 0; e < ACC_N; ++e) acc.c[i][j][e] = 0.f;
   if (nk <= 0) return;
 
-  RowFrag rf, cf;
+  typename FragOf<ROp>::type rf;
+  typename FragOf<COp>::type cf;
+  constexpr int RA = FragOf<ROp>::reads, RB = FragOf<COp>::reads;
   rf.init(wm * 128, lane);
   cf.init(wn * WAVE_COLS, lane);
   bf16x8_t fa[2][FM], fb[2][FN];
-#define DPO_RD_A(buf_, s_, slot_, i_) fa[slot_][i_] = rf.read(smem + (buf_) * STAGE_BYTES, i_, s_)
-#define DPO_RD_B(buf_, s_, slot_, j_) fb[slot_][j_] = cf.read(smem + (buf_) * STAGE_BYTES + OPER_BYTES, j_, s_)
+#define DPO_RD_A(buf_, s_, slot_, i_) fa[slot_][i_] = rf.read(DPO_STG(buf_), i_, s_)
+#define DPO_RD_B(buf_, s_, slot_, j_) fb[slot_][j_] = cf.read(DPO_STG(buf_) + OPER_BYTES, j_, s_)
 #define DPO_ROW(slot_, i_, buf_, s_)                                                                      \
   do {                                                                                                    \
     _Pragma("unroll") for (int j_ = 0; j_ < FN; ++j_) acc.c[i_][j_] =                                     \
@@ -167,23 +284,44 @@ __device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& co
     DPO_RD_A(buf_, s_, (slot_) ^ 1, i_);                                                                  \
     if ((i_) < FN) {                                                                                      \
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                                  \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);                                                 \
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                                  \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);                                                 \
     } else {                                                                                              \
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                                  \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);                                                 \
     }                                                                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                                    \
   } while (0)
+  // one stage held in buffer cur_ (K step kt_): step 0 on slot 0 (reading
+  // step 1 into slot 1), row 0 of step 1, the stage barrier, the loads two
+  // stages ahead into buffer cur_, rows 1..7 of step 1 (reading the next
+  // stage's step 0 from the other buffer into slot 0)
+#define DPO_STAGE(cur_, kt_)                                                                              \
+  do {                                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) DPO_ROW(0, i, cur_, 1);                                \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) acc.c[0][j] =                                          \
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[1][0], fb[1][j], acc.c[0][j], 0, 0, 0);                \
+    __builtin_amdgcn_sched_barrier(0);                                                                    \
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                                           \
+    __builtin_amdgcn_s_barrier();                                                                         \
+    if ((kt_) + 2 < nk) {                                                                                 \
+      load_stage(rop, (kt_) + 2, DPO_STG_LDS(cur_), wave);                                                \
+      load_stage(cop, (kt_) + 2, DPO_STG_LDS(cur_) + OPER_BYTES, wave);                                   \
+    }                                                                                                     \
+    DPO_RD_B((cur_) ^ 1, 0, 0, 0);                                                                        \
+    DPO_RD_A((cur_) ^ 1, 0, 0, 0);                                                                        \
+    __builtin_amdgcn_sched_barrier(0);                                                                    \
+    _Pragma("unroll") for (int i = 1; i < FM; ++i) DPO_ROW(1, i, (cur_) ^ 1, 0);                          \
+  } while (0)
 
-  load_stage(rop, 0, smem, wave);
-  load_stage(cop, 0, smem + OPER_BYTES, wave);
+  load_stage(rop, 0, DPO_STG_LDS(0), wave);
+  load_stage(cop, 0, DPO_STG_LDS(0) + OPER_BYTES, wave);
   wait_loads();
   __syncthreads();
   if (nk > 1) {
-    load_stage(rop, 1, smem + STAGE_BYTES, wave);
-    load_stage(cop, 1, smem + STAGE_BYTES + OPER_BYTES, wave);
+    load_stage(rop, 1, DPO_STG_LDS(1), wave);
+    load_stage(cop, 1, DPO_STG_LDS(1) + OPER_BYTES, wave);
   }
   // the loop's own read order (B_i, A_i, ...), all landed before the loop: the
   // compiler's wait counts at the loop head then follow the loop's reads only
@@ -194,26 +332,12 @@ __device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& co
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) DPO_ROW(0, i, cur, 1);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      acc.c[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[1][0], fb[1][j], acc.c[0][j], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    if (kt + 2 < nk) {
-      load_stage(rop, kt + 2, smem + cur * STAGE_BYTES, wave);
-      load_stage(cop, kt + 2, smem + cur * STAGE_BYTES + OPER_BYTES, wave);
-    }
-    DPO_RD_B(cur ^ 1, 0, 0, 0);
-    DPO_RD_A(cur ^ 1, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 1; i < FM; ++i) DPO_ROW(1, i, cur ^ 1, 0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    DPO_STAGE(0, kt);
+    if (kt + 1 >= nk) break;
+    DPO_STAGE(1, kt + 1);
   }
+#undef DPO_STAGE
 #undef DPO_ROW
 #undef DPO_RD_B
 #undef DPO_RD_A

@@ -18,9 +18,8 @@
 //   k_combine        combine of the per-tile (max, sum exp), fp64 sums -> lse, log p
 //                    (and of the per-tile logit sums, when asked for)
 //   k_row_sums       fp64 per-row sums in a fixed order
-//   k_transpose_w    W^T (bf16) for the dHidden contraction
 //   k_gather_ht      Hc^T (bf16) for the dW contraction
-//   k_dprod_gemm     recompute Z tile; epilogue D = w exp(z - lse) -> bf16 D, D^T (softmax part)
+//   k_dprod_gemm     recompute Z tile; epilogue D = w exp(z - lse) -> bf16 D (softmax part)
 //   k_dh_gemm        dHidden partials = D . W, K split in parts; each part's fp32 slab
 //                    accumulates over the vocabulary slices
 //   k_dh_finish      dHidden rows = sum of the slabs - w W[target], scattered to their positions
@@ -131,6 +130,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CompactArgs a) {
 // two cross-lane shuffles, and the two vocabulary halves of the block
 // (wm = 0, 1) meet through a small LDS table.
 constexpr int kEpiBytes = 8192;  // per-position staging + cross-wave reduction
+static __shared__ __attribute__((aligned(16))) char g_epi[kEpiBytes];
 
 template <typename F>
 __device__ __forceinline__ void for_vocab(const Acc& acc, int j, F f) {
@@ -163,10 +163,9 @@ __device__ __forceinline__ void mask_vocab_tail(Acc& acc, int vbase, int V, int 
 
 template <bool ZSUM>
 __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  int* tgt_s = (int*)(smem + PIPE_BYTES);                  // 256 ints
-  float2* red = (float2*)(smem + PIPE_BYTES + 1024);       // [2][256]
-  float* red_z = (float*)(smem + PIPE_BYTES + 5120);       // [2][256] (logit sums)
+  int* tgt_s = (int*)g_epi;                   // 256 ints
+  float2* red = (float2*)(g_epi + 1024);      // [2][256]
+  float* red_z = (float*)(g_epi + 5120);      // [2][256] (logit sums)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -183,13 +182,13 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
     // position, addressed from the start of the hidden tensor
     const RowOperand wop = row_operand(a.w + (size_t)n0 * a.H, a.H, (long)a.V - n0, 0, tid);
     RowOperand hop;
-    hop.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.hidden, (short)0, (int)a.hidden_bytes, kBufferFlags);
+    hop.rsrc = buffer_rsrc(a.hidden, a.hidden_bytes);
 #pragma unroll
     for (int it = 0; it < LOADS_PER_THREAD; ++it)
       hop.voff[it] = (unsigned)(((size_t)a.idx[m0 + row_loader_row(it, tid)] * a.H + lchunk * 8) * 2);
     if (tid < BM) tgt_s[tid] = a.tgt_c[m0 + tid];
     Acc acc;
-    mainloop(acc, wop, hop, a.H / BK, smem, wave, lane, wm, wn);
+    mainloop(acc, wop, hop, a.H / BK, wave, lane, wm, wn);
 
     const int vbase = n0 + wm * 128;  // first vocabulary row of this wave
     if (n0 + BN > a.V) mask_vocab_tail(acc, vbase, a.V, lane);
@@ -377,37 +376,8 @@ __global__ __launch_bounds__(256) void k_shard_combine(ShardCombineArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// operand transposes for the backward contractions
+// gathered hidden rows, transposed, for the dW_vocab contraction
 // ---------------------------------------------------------------------------
-// W [V, H] -> WT [H, Vp], zero columns v >= V.  64x64 tiles through LDS,
-// 16-byte global reads and writes.
-__global__ __launch_bounds__(256) void k_transpose_w(TransposeWArgs a) {
-  __shared__ uint16_t tile[64][72];
-  const int v0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int q = it * 256 + tid;        // 64 rows x 8 chunks
-    const int r = q >> 3, c = q & 7;
-    const int v = v0 + r;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (v < a.V) val = *(const u32x4*)(a.w + (size_t)v * a.H + h0 + c * 8);
-    *(u32x4*)&tile[r][c * 8] = val;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int q = it * 256 + tid;        // 64 output rows (h) x 8 chunks of 8 v
-    const int h = q >> 3, c = q & 7;
-    uint32_t w4[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      w4[u] = (uint32_t)tile[c * 8 + 2 * u][h] | ((uint32_t)tile[c * 8 + 2 * u + 1][h] << 16);
-    const u32x4 o = {w4[0], w4[1], w4[2], w4[3]};
-    *(u32x4*)(a.wt + (size_t)(h0 + h) * a.Vp + v0 + c * 8) = o;
-  }
-}
-
 // hidden rows at completion positions -> HT [H, Mp], zero columns m >= n_c.
 // 64 positions x 64 hidden columns per block, 16-byte loads and stores.
 __global__ __launch_bounds__(256) void k_gather_ht(GatherHTArgs a) {
@@ -440,25 +410,30 @@ __global__ __launch_bounds__(256) void k_gather_ht(GatherHTArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// backward: recompute Z, D = w exp(z - lse) in bf16, written in both layouts
+// backward: recompute Z, D = w exp(z - lse) in bf16
 // ---------------------------------------------------------------------------
 // Same MFMA orientation as the forward (rows = vocabulary, columns =
 // positions): a lane holds 4 consecutive vocabulary entries of one position
 // per fragment, packed to one 8-byte LDS write.  The bf16 tile (256
 // positions x 256 vocabulary, 128 KiB) is staged in the freed pipeline LDS
-// and leaves as 16-byte coalesced rows of D [Mp, Vp] and of D^T [Vp, Mp].
+// and leaves as 16-byte coalesced rows of D [Mp, Vp].  Both consumers read D
+// as it is: dHidden with K = vocabulary along its rows, dW_vocab with K =
+// positions down its columns (transposing LDS reads), so no D^T is written.
 // Staging layout: the 16-byte chunk c of position row p sits at chunk
-// c ^ f(p), f(p) = (p ^ (p >> 3)) & 31, which keeps both the row-wise
-// writes/reads and the column-wise (transposing) reads free of bank conflicts.
+// c ^ f(p), f(p) = (p ^ (p >> 3)) & 31, which keeps the 8-byte writes of the
+// four lane groups and the row reads free of bank conflicts.
 __device__ __forceinline__ int stage_off(int p, int v) {
   const int f = (p ^ (p >> 3)) & 31;
   return p * 512 + ((((v >> 3) ^ f)) << 4) + ((v & 7) << 1);
 }
+// positions 0..127 are staged in the first pipeline buffer, 128..255 in the second
+__device__ __forceinline__ char* stage_at(int p, int v) {
+  return (p < BM / 2 ? g_stage0 : g_stage1) + stage_off(p & (BM / 2 - 1), v);
+}
 
 __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  float* lse_s = (float*)(smem + PIPE_BYTES);
-  float* w_s = (float*)(smem + PIPE_BYTES + 1024);
+  float* lse_s = (float*)g_epi;
+  float* w_s = (float*)(g_epi + 1024);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -475,7 +450,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
     // position, addressed from the start of the hidden tensor
     const RowOperand wop = row_operand(a.w + (size_t)n0 * a.H, a.H, (long)a.V - n0, 0, tid);
     RowOperand hop;
-    hop.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.hidden, (short)0, (int)a.hidden_bytes, kBufferFlags);
+    hop.rsrc = buffer_rsrc(a.hidden, a.hidden_bytes);
 #pragma unroll
     for (int it = 0; it < LOADS_PER_THREAD; ++it)
       hop.voff[it] = (unsigned)(((size_t)a.idx[m0 + row_loader_row(it, tid)] * a.H + lchunk * 8) * 2);
@@ -486,7 +461,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
       w_s[tid] = live ? a.weight[a.row_c[m]] : 0.f;
     }
     Acc acc;
-    mainloop(acc, wop, hop, a.H / BK, smem, wave, lane, wm, wn);
+    mainloop(acc, wop, hop, a.H / BK, wave, lane, wm, wn);
     if (n0 + BN > a.V) mask_vocab_tail(acc, n0 + wm * 128, a.V, lane);
 
     // D values (bf16) into the staging tile; the pipeline LDS is free now
@@ -508,7 +483,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
         uint2 pk;
         pk.x = pack_bf16x2(d[0], d[1]);
         pk.y = pack_bf16x2(d[2], d[3]);
-        *(uint2*)(smem + stage_off(pl, vl)) = pk;
+        *(uint2*)stage_at(pl, vl) = pk;
       }
     }
     __syncthreads();
@@ -517,40 +492,15 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
     for (int it = 0; it < BM * 32 / NTHREADS; ++it) {
       const int g = it * NTHREADS + etid;
       const int p = g >> 5, c = g & 31;
-      const u32x4 v = *(const u32x4*)(smem + stage_off(p, c * 8));
+      const u32x4 v = *(const u32x4*)stage_at(p, c * 8);
       __builtin_nontemporal_store(v, (u32x4*)(a.D + (size_t)(m0 + p) * a.Vp + n0 + c * 8));
-    }
-    // D^T rows: vocabulary n0+v, positions m0 .. m0+255, through transposing
-    // LDS reads.  In a 16-lane group, lane L supplies the 8-byte piece
-    // (vocabulary 4*c0 .. +3) of position row P0 + 8*(L&3) + (L>>2); the read
-    // hands lane i the entries of vocabulary 4*c0 + (i&3) at positions
-    // P0 + 8*(i>>2) + 0..3.  A second read 4 rows down gives the next 4
-    // positions, so each lane ends with 8 consecutive positions (16 bytes).
-    {
-      const int grp = elane >> 4, L = elane & 15;
-#pragma unroll 2
-      for (int it = 0; it < BN * BM / (8 * NTHREADS); ++it) {
-        const int u = it * (NTHREADS / 64) + wave;  // 0 .. 127
-        const int c0 = u & 63;                      // vocabulary quad
-        const int P0 = (u >> 6) * 128 + 32 * grp;   // first position of this lane group
-        const int prow = P0 + 8 * (L & 3) + (L >> 2);
-        const i16x4_t A = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(smem + stage_off(prow, 4 * c0)));
-        const i16x4_t B = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(smem + stage_off(prow + 4, 4 * c0)));
-        const int v = 4 * c0 + (L & 3);
-        const int P = P0 + 8 * (L >> 2);
-        const u32x4 o = {(uint32_t)(uint16_t)A[0] | ((uint32_t)(uint16_t)A[1] << 16),
-                         (uint32_t)(uint16_t)A[2] | ((uint32_t)(uint16_t)A[3] << 16),
-                         (uint32_t)(uint16_t)B[0] | ((uint32_t)(uint16_t)B[1] << 16),
-                         (uint32_t)(uint16_t)B[2] | ((uint32_t)(uint16_t)B[3] << 16)};
-        __builtin_nontemporal_store(o, (u32x4*)(a.DT + (size_t)(n0 + v) * a.ldt + m0 + P));
-      }
     }
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// dHidden = D . W  (R = D rows, C = W^T rows), K = the slice's vocabulary
+// dHidden = D . W  (R = D rows, C = W read K-major), K = the slice's vocabulary
 // split in dh_splits() parts.  Part ks of every slice accumulates into fp32
 // slab ks (the first slice writes it, later ones add to it: the slices run in
 // stream order, so the order of the additions is fixed); k_dh_finish adds the
@@ -583,18 +533,22 @@ __device__ __forceinline__ int dh_splits(int n_c, int H, int nkt, int grid, int 
 __device__ __forceinline__ size_t dh_slab(int n_c, int H) { return (size_t)cdiv(n_c, BM) * BM * H; }
 
 // The fp32 tile leaves through LDS in two halves of 128 rows (the pipeline
-// buffers are free after the main loop): the waves owning a half write their
+// buffers, free after the main loop, hold 64 rows each): the waves owning a half write their
 // accumulators into a 128 x 256 float table (16-column blocks XOR-swizzled by
 // row so the four row groups of a wave's write land in distinct banks), then
 // all threads move it as 16-byte vectors, one 1 KiB row per wave.  With
-// `accumulate`, the slab's current values of the half are loaded first (16
-// coalesced loads per thread in flight together) and the sums stored.
+// `accumulate`, the slab's current values are loaded first, 8 coalesced
+// loads per thread in flight together, and the sums stored.
 __device__ __forceinline__ int dh_stage_col(int row, int col) { return col ^ (((row >> 2) & 3) << 4); }
+// row r of a half: rows 0..63 in the first pipeline buffer, 64..127 in the second
+__device__ __forceinline__ float* dh_stage(int row) {
+  return (float*)(row < 64 ? g_stage0 : g_stage1) + (row & 63) * BN;
+}
 
 __device__ __forceinline__ void dh_store_tile(const Acc& acc, float* part, int m0, int n0, int n_c, int H,
-                                              int accumulate, char* smem, int tid, int lane, int wm, int wn) {
-  float* stage = (float*)smem;
+                                              int accumulate, int tid, int lane, int wm, int wn) {
   constexpr int kIters = (BM / 2) * BN / 4 / NTHREADS;  // 16 float4 per thread per half
+  constexpr int kBatch = 8;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     if (wm == h) {
@@ -605,41 +559,44 @@ __device__ __forceinline__ void dh_store_tile(const Acc& acc, float* part, int m
           const int row = i * FRAG + 4 * (lane >> 4) + e;
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            stage[row * BN + dh_stage_col(row, acc_col(wn, j, lane))] = acc.c[i][j][e];
+            dh_stage(row)[dh_stage_col(row, acc_col(wn, j, lane))] = acc.c[i][j][e];
         }
     }
     __syncthreads();
-    float4 old[kIters];
-    if (accumulate) {
+    // two batches of 8 vectors: 8 coalesced loads in flight per thread
 #pragma unroll
-      for (int it = 0; it < kIters; ++it) {
-        const int g = it * NTHREADS + tid;
+    for (int b = 0; b < kIters; b += kBatch) {
+      float4 old[kBatch];
+      if (accumulate) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int g = (b + u) * NTHREADS + tid;
+          const int row = g >> 6, c4 = g & 63;
+          const int m = m0 + h * (BM / 2) + row, col = n0 + c4 * 4;
+          old[u] = (m < n_c && col < H) ? *(const float4*)(part + (size_t)m * H + col)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int g = (b + u) * NTHREADS + tid;
         const int row = g >> 6, c4 = g & 63;
         const int m = m0 + h * (BM / 2) + row, col = n0 + c4 * 4;
-        old[it] = (m < n_c && col < H) ? *(const float4*)(part + (size_t)m * H + col)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 v = *(const float4*)(dh_stage(row) + dh_stage_col(row, c4 * 4));
+        if (accumulate) {
+          v.x += old[u].x;
+          v.y += old[u].y;
+          v.z += old[u].z;
+          v.w += old[u].w;
+        }
+        if (m < n_c && col < H) *(float4*)(part + (size_t)m * H + col) = v;
       }
-    }
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int g = it * NTHREADS + tid;
-      const int row = g >> 6, c4 = g & 63;
-      const int m = m0 + h * (BM / 2) + row, col = n0 + c4 * 4;
-      float4 v = *(const float4*)(stage + row * BN + dh_stage_col(row, c4 * 4));
-      if (accumulate) {
-        v.x += old[it].x;
-        v.y += old[it].y;
-        v.z += old[it].z;
-        v.w += old[it].w;
-      }
-      if (m < n_c && col < H) *(float4*)(part + (size_t)m * H + col) = v;
     }
     __syncthreads();
   }
 }
 
 __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -660,11 +617,11 @@ __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
     const int kb = ks * nks;
     const int nk = max(0, min(nks, nkt - kb));
     const RowOperand dop = row_operand(a.D + (size_t)m0 * a.Vp, a.Vp, (long)a.Mp - m0, kb * BK, tid);
-    const RowOperand wop = row_operand(a.wt + (size_t)n0 * a.ldw, a.ldw, (long)a.H - n0, kb * BK, tid);
+    const KOperand wop = kmajor_operand(a.w + (size_t)kb * BK * a.H + n0, a.H, (long)a.V - kb * BK, tid);
     Acc acc;
-    mainloop(acc, dop, wop, nk, smem, wave, lane, wm, wn);
+    mainloop(acc, dop, wop, nk, wave, lane, wm, wn);
     float* part = a.part + (size_t)ks * slab;
-    dh_store_tile(acc, part, m0, n0, n_c, a.H, a.accumulate, smem, opaque(tid), opaque(lane), wm, wn);
+    dh_store_tile(acc, part, m0, n0, n_c, a.H, a.accumulate, opaque(tid), opaque(lane), wm, wn);
     __syncthreads();
   }
 }
@@ -699,10 +656,9 @@ __global__ __launch_bounds__(256) void k_dh_finish(DhFinishArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dW_vocab = D^T . Hc  (R = D^T rows, C = Hc^T rows), K = completion positions
+// dW_vocab = D^T . Hc  (R = D read K-major, C = Hc^T rows), K = completion positions
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -715,10 +671,10 @@ __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
     int mt, nt;
     sc.coords(t, mt, nt);
     const int m0 = mt * BM, n0 = nt * BN;
-    const RowOperand dop = row_operand(a.DT + (size_t)m0 * a.ldt, a.ldt, (long)a.Vp - m0, 0, tid);
+    const KOperand dop = kmajor_operand(a.D + m0, a.Vp, (long)align_up((size_t)n_c, BM), tid);
     const RowOperand hop = row_operand(a.ht + (size_t)n0 * a.ldt, a.ldt, (long)a.H - n0, 0, tid);
     Acc acc;
-    mainloop(acc, dop, hop, nk, smem, wave, lane, wm, wn);
+    mainloop(acc, dop, hop, nk, wave, lane, wm, wn);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -999,43 +955,19 @@ __global__ __launch_bounds__(256) void k_zero_rows(ZeroRowsArgs a) {
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-static int gemm_lds_bytes() { return PIPE_BYTES + kEpiBytes; }
-
-// The 136 KiB of dynamic LDS needs an opt-in per kernel.  It is set once per
-// (kernel, device), on the first launch from a thread whose current device
-// is that device.
-static hipError_t prep_gemm(const void* fn) {
-  constexpr int kMaxDev = 64, kMaxFn = 8;
-  static std::mutex mu;
-  static const void* fns[kMaxFn] = {};
-  static bool done[kMaxFn][kMaxDev] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> g(mu);
-  int slot = 0;
-  while (slot < kMaxFn && fns[slot] && fns[slot] != fn) ++slot;
-  if (slot == kMaxFn) return hipErrorUnknown;
-  fns[slot] = fn;
-  if (done[slot][dev]) return hipSuccess;
-  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes());
-  if (e == hipSuccess) done[slot][dev] = true;
-  return e;
-}
-
+// The contractions' LDS (two 64 KiB stage buffers and the 8 KiB epilogue
+// area, 136 KiB of the 160 KiB a CU has) is static, part of each kernel's
+// code object: nothing is set up at launch.
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_gemm(const FwdArgs& a, int grid, hipStream_t s) {
-  const hipError_t e = prep_gemm(a.part_z ? (const void*)k_fwd_gemm<true> : (const void*)k_fwd_gemm<false>);
-  if (e != hipSuccess) return e;
   if (a.part_z)
-    hipLaunchKernelGGL(k_fwd_gemm<true>, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+    hipLaunchKernelGGL(k_fwd_gemm<true>, dim3(grid), dim3(NTHREADS), 0, s, a);
   else
-    hipLaunchKernelGGL(k_fwd_gemm<false>, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+    hipLaunchKernelGGL(k_fwd_gemm<false>, dim3(grid), dim3(NTHREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1059,20 +991,13 @@ hipError_t launch_row_sums(const RowSumArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_transpose_w(const TransposeWArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_transpose_w, dim3(a.Vp / 64, a.H / 64), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_gather_ht(const GatherHTArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_gather_ht, dim3(a.Mp / 64, a.H / 64), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dprod_gemm(const DProdArgs& a, int grid, hipStream_t s) {
-  const hipError_t e = prep_gemm((const void*)k_dprod_gemm);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_dprod_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+  hipLaunchKernelGGL(k_dprod_gemm, dim3(grid), dim3(NTHREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1082,16 +1007,12 @@ hipError_t launch_dh_finish(const DhFinishArgs& a, int Mp, hipStream_t s) {
 }
 
 hipError_t launch_dh_gemm(const DhArgs& a, int grid, hipStream_t s) {
-  const hipError_t e = prep_gemm((const void*)k_dh_gemm);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_dh_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+  hipLaunchKernelGGL(k_dh_gemm, dim3(grid), dim3(NTHREADS), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dw_gemm(const DwArgs& a, int grid, hipStream_t s) {
-  const hipError_t e = prep_gemm((const void*)k_dw_gemm);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_dw_gemm, dim3(grid), dim3(NTHREADS), gemm_lds_bytes(), s, a);
+  hipLaunchKernelGGL(k_dw_gemm, dim3(grid), dim3(NTHREADS), 0, s, a);
   return hipGetLastError();
 }
 

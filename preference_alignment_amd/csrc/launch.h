@@ -93,12 +93,6 @@ struct RowSumArgs {
   int32_t* n_tokens;  // nullable
 };
 
-struct TransposeWArgs {
-  const uint16_t* w;
-  int V, H, Vp;
-  uint16_t* wt;  // [H, Vp]
-};
-
 struct GatherHTArgs {
   const uint16_t* hidden;
   const int* idx;
@@ -119,14 +113,12 @@ struct DProdArgs {
   const float* lse;     // [rows*T] from the forward
   const float* weight;  // [rows]
   uint16_t* D;          // [Mp, Vp] bf16
-  uint16_t* DT;         // [Vp, ldt] bf16
-  int ldt;              // row stride of D^T (positions, padded)
 };
 
 struct DhArgs {
   const uint16_t* D;    // [Mp, Vp] the slice's D
-  const uint16_t* wt;   // [H, ldw] W^T, offset to the slice's first vocabulary column
-  int H, V, Vp, ldw, Mp, gm;
+  const uint16_t* w;    // [V, H] the slice's rows of W_vocab, read K-major (K = vocabulary)
+  int H, V, Vp, Mp, gm;
   int max_split;  // the kernel splits K into dh_splits(...) <= this many parts
   int nkt_ref;    // K steps of the first slice: every slice and the finish choose the same split count
   int accumulate;  // 0: the first slice writes the slabs; 1: later slices add to them
@@ -177,7 +169,7 @@ struct OnehotDwArgs {
 };
 
 struct DwArgs {
-  const uint16_t* DT;   // [Vp, ldt]
+  const uint16_t* D;    // [Mp, Vp] the slice's D, read K-major (K = positions)
   const uint16_t* ht;   // [H, ldt]
   int V, H, Vp, Mp, ldt, gm, accumulate;
   const WsHeader* hdr;
@@ -245,7 +237,6 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 hipError_t launch_fwd_gemm(const FwdArgs& a, int grid, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_row_sums(const RowSumArgs& a, hipStream_t s);
-hipError_t launch_transpose_w(const TransposeWArgs& a, hipStream_t s);
 hipError_t launch_gather_ht(const GatherHTArgs& a, hipStream_t s);
 hipError_t launch_dprod_gemm(const DProdArgs& a, int grid, hipStream_t s);
 hipError_t launch_dh_gemm(const DhArgs& a, int grid, hipStream_t s);
