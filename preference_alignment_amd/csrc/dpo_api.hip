@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <numeric>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -31,7 +32,9 @@ constexpr int kMaxSplitDh = 4;
 // The backward holds the bf16 softmax part of dlogits (D) only for one slice
 // of the vocabulary at a time: D stays under this many bytes (balanced slices
 // of whole 256-wide tiles).
-constexpr size_t kChunkBytes = size_t(1) << 30;
+constexpr size_t kChunkBytes = size_t(2) << 30;
+// output tiles one round of the persistent contractions covers (one per CU of MI355X)
+constexpr int kRoundTiles = 256;
 constexpr int kTransPad = 64;  // elements
 // workgroups per CU of the chunked streaming backward
 constexpr int kStreamBwdBlocksPerCU = 32;
@@ -140,8 +143,12 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
   if (op == DPO_OP_HEAD_BACKWARD) {
     const size_t tile_bytes = (size_t)L.Mp * gemm::BN * 2;
     const int max_tiles = (int)std::max<size_t>(1, std::min<size_t>(L.nVt, kChunkBytes / tile_bytes));
-    L.n_chunks = cdiv(L.nVt, max_tiles);
-    L.chunk_tiles = cdiv(L.nVt, L.n_chunks);
+    // whole slices of a multiple of q tiles, so that a slice's dW contraction
+    // (slice tiles x H / 256 output tiles) fills whole rounds of the CUs
+    const int nNt = cdiv(H, gemm::BN);
+    const int q = kRoundTiles / std::gcd(kRoundTiles, nNt);
+    L.chunk_tiles = max_tiles >= L.nVt ? L.nVt : (max_tiles >= q ? max_tiles / q * q : max_tiles);
+    L.n_chunks = cdiv(L.nVt, L.chunk_tiles);
     const size_t Vcp = (size_t)L.chunk_tiles * gemm::BN;
     // Hc^T rows are positions long; a pad of 128 bytes keeps their stride off
     // a power of two (2^15 bytes at 16,384 positions), where all rows of a

@@ -675,20 +675,9 @@ __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
     const RowOperand hop = row_operand(a.ht + (size_t)n0 * a.ldt, a.ldt, (long)a.H - n0, 0, tid);
     Acc acc;
     mainloop(acc, dop, hop, nk, wave, lane, wm, wn);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int e = 0; e < ACC_N; ++e) {
-        const int v = m0 + acc_row(wm, i, e, lane);
-        if (v >= a.V) continue;
-        float* dst = a.d_w + (size_t)v * a.H;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + acc_col(wn, j, lane);
-          if (col < a.H) dst[col] = a.accumulate ? dst[col] + acc.c[i][j][e] : acc.c[i][j][e];
-        }
-      }
-    }
+    // written (or added, with accumulate) through the same coalesced path as
+    // the dHidden partials: rows = vocabulary, row length H
+    dh_store_tile(acc, a.d_w, m0, n0, a.V, a.H, a.accumulate, opaque(tid), opaque(lane), wm, wn);
     __syncthreads();
   }
 }
