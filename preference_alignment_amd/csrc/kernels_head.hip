@@ -656,8 +656,68 @@ __global__ __launch_bounds__(256) void k_dh_finish(DhFinishArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dW_vocab = D^T . Hc  (R = D read K-major, C = Hc^T rows), K = completion positions
+// dW_vocab = D^T . Hc, K = completion positions, computed as its transpose
+// (R = Hc^T rows, C = D read K-major)
 // ---------------------------------------------------------------------------
+// dW tile with exchanged roles: MFMA rows = hidden columns h, columns =
+// vocabulary rows v, so the K-major operand (D) supplies the 4 column
+// fragments (8 transposing reads per K step instead of 16).  The tile is
+// transposed on its way out: waves holding vocabulary rows [128 hv, 128 hv +
+// 128) write T[v][h..h+3] as 16-byte LDS writes (chunk c of row v at c ^ (v &
+// 15): the 16 rows of a lane group land in distinct banks), then every thread
+// moves 16-byte vectors of T's rows to dW[v][h].
+__device__ __forceinline__ float* dwt_row(int v) {
+  return (float*)(v < 64 ? g_stage0 : g_stage1) + (v & 63) * BM;
+}
+__device__ __forceinline__ void dwt_store_tile(const Acc& acc, float* dw, int h0, int v0, int V, int H, int accumulate,
+                                               int tid, int lane, int wm, int wn) {
+  constexpr int kIters = (BN / 2) * BM / 4 / NTHREADS;  // 16 float4 per thread per half
+  constexpr int kBatch = 8;
+#pragma unroll
+  for (int hv = 0; hv < 2; ++hv) {
+    if ((wn >> 1) == hv) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int v = acc_col(wn, j, lane) - hv * (BN / 2);  // 0..127
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int c = (acc_row(wm, i, 0, lane)) >> 2;     // h chunk of 4
+          *(floatx4*)(dwt_row(v) + ((c ^ (v & 15)) << 2)) = acc.c[i][j];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < kIters; b += kBatch) {
+      float4 old[kBatch];
+      if (accumulate) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int g = (b + u) * NTHREADS + tid;
+          const int v = g >> 6, c4 = g & 63;
+          const int vv = v0 + hv * (BN / 2) + v, col = h0 + c4 * 4;
+          old[u] = (vv < V && col < H) ? *(const float4*)(dw + (size_t)vv * H + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int g = (b + u) * NTHREADS + tid;
+        const int v = g >> 6, c4 = g & 63;
+        const int vv = v0 + hv * (BN / 2) + v, col = h0 + c4 * 4;
+        float4 x = *(const float4*)(dwt_row(v) + ((c4 ^ (v & 15)) << 2));
+        if (accumulate) {
+          x.x += old[u].x;
+          x.y += old[u].y;
+          x.z += old[u].z;
+          x.w += old[u].w;
+        }
+        if (vv < V && col < H) *(float4*)(dw + (size_t)vv * H + col) = x;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -666,19 +726,16 @@ __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
   const int n_c = a.hdr->n_c;
   const int nk = cdiv(n_c, BK);
   Sched sc;
-  sc.init(a.Vp / BM, cdiv(a.H, BN), a.gm);
+  sc.init(cdiv(a.H, BM), a.Vp / BN, a.gm);
   for (int t = sc.begin; t < sc.end; t += sc.step) {
     int mt, nt;
     sc.coords(t, mt, nt);
-    const int m0 = mt * BM, n0 = nt * BN;
-    const KOperand dop = kmajor_operand(a.D + m0, a.Vp, (long)align_up((size_t)n_c, BM), tid);
-    const RowOperand hop = row_operand(a.ht + (size_t)n0 * a.ldt, a.ldt, (long)a.H - n0, 0, tid);
+    const int h0 = mt * BM, v0 = nt * BN;
+    const RowOperand hop = row_operand(a.ht + (size_t)h0 * a.ldt, a.ldt, (long)a.H - h0, 0, tid);
+    const KOperand dop = kmajor_operand(a.D + v0, a.Vp, (long)align_up((size_t)n_c, BM), tid);
     Acc acc;
-    mainloop(acc, dop, hop, nk, wave, lane, wm, wn);
-    // written (or added, with accumulate) through the same coalesced path as
-    // the dHidden partials: rows = vocabulary, row length H
-    dh_store_tile(acc, a.d_w, m0, n0, a.V, a.H, a.accumulate, opaque(tid), opaque(lane), wm, wn);
-    __syncthreads();
+    mainloop(acc, hop, dop, nk, wave, lane, wm, wn);
+    dwt_store_tile(acc, a.d_w, h0, v0, a.V, a.H, a.accumulate, opaque(tid), opaque(lane), wm, wn);
   }
 }
 
