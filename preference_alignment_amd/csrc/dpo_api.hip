@@ -86,6 +86,13 @@ struct Layout {
   size_t D = 0, HT = 0;
   size_t keysA = 0, valsA = 0, keysB = 0, valsB = 0, dhpart = 0, spos = 0, sw = 0, ohcont = 0, ohhead = 0;
   size_t total = 0;
+#ifdef DPO_HOST_CHECKS
+  // every region the layout hands out (offset, bytes), for the host-side checks
+  struct Region {
+    size_t at, bytes;
+  } regions[32];
+  int n_regions = 0;
+#endif
 };
 
 bool op_needs_h(int op) {
@@ -116,6 +123,9 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
   auto take = [&](size_t bytes) {
     const size_t at = o;
     o = align_up(o + bytes, A);
+#ifdef DPO_HOST_CHECKS
+    if (L.n_regions < 32) L.regions[L.n_regions++] = {at, bytes};
+#endif
     return at;
   };
   L.hdr = take(sizeof(WsHeader));

@@ -353,6 +353,31 @@ __device__ __forceinline__ int acc_row(int wm, int i, int e, int lane) {
 }
 __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * WAVE_COLS + j * FRAG + (lane & 15); }
 
+// The dHidden contraction has few output tiles (positions x H), so K (the
+// slice's vocabulary) is split to fill the CUs: the split count minimises
+// rounds of tiles over the grid times K steps per tile (ties to fewer parts),
+// among the counts whose slabs (align(n_c, 256) x H floats each) fit in the
+// 2 Mp x H floats the workspace holds.  It depends on N_c, which only the
+// device knows; the finish recomputes it.
+__host__ __device__ inline int dh_splits(int n_c, int H, int nkt, int grid, int max_split, int Mp) {
+  const int mt = cdiv(n_c, BM);
+  const long tiles = (long)mt * cdiv(H, BN);
+  const long cap = mt > 0 ? (2L * Mp) / ((long)mt * BM) : max_split;
+  int best = 1;
+  long best_cost = -1;
+  for (int s = 1; s <= max_split && s <= (nkt > 1 ? nkt : 1) && s <= cap; ++s) {
+    const long cost = (tiles * s + grid - 1) / grid * cdiv(nkt, s);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
+
+// slab ks of the dHidden partial sums: align(n_c, BM) rows of H floats each
+__host__ __device__ inline size_t dh_slab(int n_c, int H) { return (size_t)cdiv(n_c, BM) * BM * H; }
+
 // Persistent tile scheduler.  Tiles are numbered in grouped order (GM m-tiles
 // wide, m fastest, then n) and the numbering is cut into NUM_XCD contiguous
 // parts; the blocks resident on one XCD (blockIdx % NUM_XCD) walk their part

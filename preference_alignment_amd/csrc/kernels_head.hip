@@ -507,30 +507,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
 // slabs in a fixed order, applies the exact one-hot term and scatters rows to
 // their positions.
 // ---------------------------------------------------------------------------
-// The dHidden contraction has few output tiles (positions x H), so K (the
-// slice's vocabulary) is split to fill the CUs: the split count minimises
-// rounds of tiles over the grid times K steps per tile (ties to fewer parts),
-// among the counts whose slabs (align(n_c, 256) x H floats each) fit in the
-// 2 Mp x H floats the workspace holds.  It depends on N_c, which only the
-// device knows; the finish recomputes it.
-__device__ __forceinline__ int dh_splits(int n_c, int H, int nkt, int grid, int max_split, int Mp) {
-  const int mt = cdiv(n_c, BM);
-  const long tiles = (long)mt * cdiv(H, BN);
-  const int cap = mt > 0 ? (2 * Mp) / (mt * BM) : max_split;
-  int best = 1;
-  long best_cost = -1;
-  for (int s = 1; s <= max_split && s <= max(nkt, 1) && s <= cap; ++s) {
-    const long cost = (tiles * s + grid - 1) / grid * cdiv(nkt, s);
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      best = s;
-    }
-  }
-  return best;
-}
 
-// slab ks of the dHidden partial sums: align(n_c, BM) rows of H floats each
-__device__ __forceinline__ size_t dh_slab(int n_c, int H) { return (size_t)cdiv(n_c, BM) * BM * H; }
 
 // The fp32 tile leaves through LDS in two halves of 128 rows (the pipeline
 // buffers, free after the main loop, hold 64 rows each): the waves owning a half write their
