@@ -1,12 +1,12 @@
 // bf16 MFMA main loop shared by the four LM-head contractions (gfx950).
 //
-// C[i][j] = sum_k R[i][k] * C[j][k]: both operands are K-contiguous in memory.
-// The kernels that use this core differ in their operands and epilogues:
+// C[i][j] = sum_k R[i][k] * C[j][k].  An operand is either ROW (its tile rows
+// are K-contiguous in memory) or K-MAJOR (contiguous along the MFMA dimension,
+// read through transposing LDS reads).  The kernels that use this core differ
+// in their operands and epilogues:
 //   forward / recompute : R = W_vocab rows, C = hidden rows at completion positions
-//   dHidden             : R = D rows (K = vocabulary), C = W_vocab^T rows
-//   dW_vocab            : R = D^T rows (K = positions), C = gathered hidden^T rows
-// (the backward writes D^T and W^T so that every operand is K-contiguous: an
-// LDS-transposed read of D for dW_vocab measured 40 % slower).
+//   dHidden             : R = D rows (K = vocabulary), C = W_vocab read K-major
+//   dW_vocab (as dW^T)  : R = gathered hidden^T rows (K = positions), C = D read K-major
 //
 // Block tile 256x256x64, 512 threads = 8 waves in a 2x4 grid (two waves per
 // SIMD, so one wave's LDS and barrier waits are covered by the other's MFMAs);
