@@ -256,9 +256,26 @@ struct FragOf<KOperand> {
 // stage those reads fetch unused values from the idle buffer, which keeps
 // the loop free of branches inside the MFMA stream.  The loop body is
 // written twice, once per buffer of the pair.
+//
+// mainloop() issues a tile's first stage, waits for it, issues the second
+// and runs the loop.  A kernel whose epilogue leaves the stage buffers alone
+// can instead issue the next tile's first two stages with mainloop_issue()
+// as soon as mainloop_prefetched() has returned (every wave is then done
+// reading them), so that their loads land while the epilogue runs.
 template <typename ROp, typename COp>
-__device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& cop, int nk, int wave, int lane,
-                                         int wm, int wn) {
+__device__ __forceinline__ void mainloop_issue(const ROp& rop, const COp& cop, int nk, int wave) {
+  if (nk <= 0) return;
+  load_stage(rop, 0, DPO_STG_LDS(0), wave);
+  load_stage(cop, 0, DPO_STG_LDS(0) + OPER_BYTES, wave);
+  if (nk > 1) {
+    load_stage(rop, 1, DPO_STG_LDS(1), wave);
+    load_stage(cop, 1, DPO_STG_LDS(1) + OPER_BYTES, wave);
+  }
+}
+// PRE: the first two stages were issued by mainloop_issue()
+template <bool PRE, typename ROp, typename COp>
+__device__ __forceinline__ void mainloop_impl(Acc& acc, const ROp& rop, const COp& cop, int nk, int wave, int lane,
+                                              int wm, int wn) {
   static_assert(FN <= FM, "B fragments are read behind the first FN rows");
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -315,11 +332,13 @@ __device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& co
     _Pragma("unroll") for (int i = 1; i < FM; ++i) DPO_ROW(1, i, (cur_) ^ 1, 0);                          \
   } while (0)
 
-  load_stage(rop, 0, DPO_STG_LDS(0), wave);
-  load_stage(cop, 0, DPO_STG_LDS(0) + OPER_BYTES, wave);
+  if (!PRE) {
+    load_stage(rop, 0, DPO_STG_LDS(0), wave);
+    load_stage(cop, 0, DPO_STG_LDS(0) + OPER_BYTES, wave);
+  }
   wait_loads();
   __syncthreads();
-  if (nk > 1) {
+  if (!PRE && nk > 1) {
     load_stage(rop, 1, DPO_STG_LDS(1), wave);
     load_stage(cop, 1, DPO_STG_LDS(1) + OPER_BYTES, wave);
   }
@@ -344,6 +363,16 @@ __device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& co
   // every wave is done with the LDS tiles before the caller reuses them
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __syncthreads();
+}
+template <typename ROp, typename COp>
+__device__ __forceinline__ void mainloop(Acc& acc, const ROp& rop, const COp& cop, int nk, int wave, int lane,
+                                         int wm, int wn) {
+  mainloop_impl<false>(acc, rop, cop, nk, wave, lane, wm, wn);
+}
+template <typename ROp, typename COp>
+__device__ __forceinline__ void mainloop_prefetched(Acc& acc, const ROp& rop, const COp& cop, int nk, int wave,
+                                                    int lane, int wm, int wn) {
+  mainloop_impl<true>(acc, rop, cop, nk, wave, lane, wm, wn);
 }
 
 // Row (within the 256-row block tile) and column (within the 256-col tile) of

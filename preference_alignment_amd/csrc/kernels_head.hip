@@ -174,21 +174,49 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
   Sched sc;
   sc.init(cdiv(n_c, BM), cdiv(a.V, BN), a.gm);
   const int lchunk = row_lchunk(tid);
+  const int nk = a.H / BK;
+  // operands of a tile: W rows n0 .. n0+255 (rows past V read as zero);
+  // hidden rows gathered by position, addressed from the start of the hidden
+  // tensor.  Each tile's stages are issued before the previous tile's epilogue.
+  RowOperand wop, hop;
+  hop.rsrc = buffer_rsrc(a.hidden, a.hidden_bytes);
+  int tgt_cur = 0;
+  if (sc.begin < sc.end) {
+    int mt, nt;
+    sc.coords(sc.begin, mt, nt);
+    const int m0 = mt * BM, n0 = nt * BN;
+    wop = row_operand(a.w + (size_t)n0 * a.H, a.H, (long)a.V - n0, 0, tid);
+#pragma unroll
+    for (int it = 0; it < LOADS_PER_THREAD; ++it)
+      hop.voff[it] = (unsigned)(((size_t)a.idx[m0 + row_loader_row(it, tid)] * a.H + lchunk * 8) * 2);
+    if (tid < BM) tgt_cur = a.tgt_c[m0 + tid];
+    mainloop_issue(wop, hop, nk, wave);
+  }
   for (int t = sc.begin; t < sc.end; t += sc.step) {
     int mt, nt;
     sc.coords(t, mt, nt);
     const int m0 = mt * BM, n0 = nt * BN;
-    // W rows n0 .. n0+255 (rows past V read as zero); hidden rows gathered by
-    // position, addressed from the start of the hidden tensor
-    const RowOperand wop = row_operand(a.w + (size_t)n0 * a.H, a.H, (long)a.V - n0, 0, tid);
-    RowOperand hop;
-    hop.rsrc = buffer_rsrc(a.hidden, a.hidden_bytes);
+    if (tid < BM) tgt_s[tid] = tgt_cur;
+    // the next tile's position indices and targets, in flight during the main loop
+    const int tn = t + sc.step;
+    const bool has_next = tn < sc.end;
+    int mtn = 0, ntn = 0;
+    if (has_next) sc.coords(tn, mtn, ntn);
+    int idx_n[LOADS_PER_THREAD];
+    int tgt_n = 0;
 #pragma unroll
-    for (int it = 0; it < LOADS_PER_THREAD; ++it)
-      hop.voff[it] = (unsigned)(((size_t)a.idx[m0 + row_loader_row(it, tid)] * a.H + lchunk * 8) * 2);
-    if (tid < BM) tgt_s[tid] = a.tgt_c[m0 + tid];
+    for (int it = 0; it < LOADS_PER_THREAD; ++it) idx_n[it] = has_next ? a.idx[mtn * BM + row_loader_row(it, tid)] : 0;
+    if (has_next && tid < BM) tgt_n = a.tgt_c[mtn * BM + tid];
     Acc acc;
-    mainloop(acc, wop, hop, a.H / BK, wave, lane, wm, wn);
+    mainloop_prefetched(acc, wop, hop, nk, wave, lane, wm, wn);
+    if (has_next) {
+      wop = row_operand(a.w + (size_t)ntn * BN * a.H, a.H, (long)a.V - ntn * BN, 0, tid);
+#pragma unroll
+      for (int it = 0; it < LOADS_PER_THREAD; ++it)
+        hop.voff[it] = (unsigned)(((size_t)idx_n[it] * a.H + lchunk * 8) * 2);
+      tgt_cur = tgt_n;
+      mainloop_issue(wop, hop, nk, wave);
+    }
 
     const int vbase = n0 + wm * 128;  // first vocabulary row of this wave
     if (n0 + BN > a.V) mask_vocab_tail(acc, vbase, a.V, lane);
