@@ -124,6 +124,8 @@ def parse():
     p.add_argument("--profile-steps", type=int, default=2,
                    help="untimed steps with every kernel timed, run before the timed region")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
+    p.add_argument("--no-also", action="store_true",
+                   help="skip the logits-path measurement that the default workload-2 run adds under 'also'")
     p.add_argument("--row", default="main", choices=ROWS,
                    help="main: the fused step (or the streaming step for workload 5); loss-variant: "
                         "length-normalised loss with an NLL term (alpha 1); vocab-shard: one GPU's quarter "
@@ -198,13 +200,17 @@ class HeadStep:
 
 
 class LogitsStep:
-    def __init__(self, x, dev):
+    def __init__(self, x, dev, logits_dev=None):
         import torch
         from preference_alignment_amd import dpo_head as D
         self.D, self.x = D, x
         R, T, V = x.rows, x.T, x.V
-        self.f32 = x.logits.dtype == np.float32
-        self.logits = torch.from_numpy(x.logits).to(dev) if self.f32 else bf(x.logits, dev)
+        if logits_dev is not None:
+            self.f32 = logits_dev.dtype == torch.float32
+            self.logits = logits_dev
+        else:
+            self.f32 = x.logits.dtype == np.float32
+            self.logits = torch.from_numpy(x.logits).to(dev) if self.f32 else bf(x.logits, dev)
         fwd = D.dpo_logits_f32_seq_logps if self.f32 else D.dpo_logits_seq_logps
         self.fwd, self.bwd = fwd, (D.dpo_logits_f32_backward if self.f32 else D.dpo_logits_backward)
         self.targets = torch.from_numpy(x.targets).to(dev)
@@ -278,6 +284,70 @@ class ShardStep:
         D.dpo_loss(self.s64, self.ref, x.beta, x.layout, self.loss, self.weight)
         D.dpo_head_backward_shard(self.hidden, self.w_shard, self.targets, self.mask, 0, x.V, self.lse,
                                   self.weight, self.dh, self.dw, 0, workspace=self.ws_b)
+
+
+def logits_workload_on_device(dev, seed=5):
+    """Workload 5's shapes, mask and targets (host generator), with its
+    N(0, 3) bf16 logits drawn on the GPU from a seeded torch generator, so
+    that the default run can also time the logits path in seconds."""
+    import torch
+    from preference_alignment_amd import workloads as W
+    _, kw = W.WORKLOADS[5]
+    R, T, V, c0, std = kw["rows"], kw["T"], kw["V"], kw["comp_start"], kw["logit_std"]
+    rng = np.random.default_rng(seed)
+    mask = np.zeros((R, T), dtype=np.uint8)
+    mask[:, c0:] = 1
+    targets = np.where(mask != 0, rng.integers(0, V, size=(R, T), dtype=np.int32), W.IGNORE_INDEX).astype(np.int32)
+    x = W.HeadInputs(name="workload5-device", rows=R, T=T, H=0, V=V, beta=0.1, layout=W.PAIRS_ADJACENT,
+                     targets=targets, mask=mask, ref_noise=rng.standard_normal(R))
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    logits = torch.empty(R, T, V, dtype=torch.bfloat16, device=dev)
+    for r in range(R):
+        logits[r] = (torch.randn(T, V, generator=g, device=dev) * std).to(torch.bfloat16)
+    return x, logits
+
+
+def also_logits_path(dev, steps=20, warmup=3):
+    """The materialised-logits path (workload 5's shape) timed the same way as
+    the main line: per-step events, then an untimed pass for the kernel split."""
+    import torch
+    from preference_alignment_amd import dpo_head as D
+    x, logits = logits_workload_on_device(dev)
+    runner = LogitsStep(x, dev, logits_dev=logits)
+    for _ in range(warmup):
+        runner.step()
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        runner.step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    med = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+    D.dpo_profile_select(None)
+    D.dpo_profile_enable(True)
+    for _ in range(2):
+        runner.step()
+    torch.cuda.synchronize()
+    kern = D.dpo_profile_read()
+    D.dpo_profile_enable(False)
+    n_c, V, E = x.n_completion, x.V, x.rows * x.T * x.V
+    step_bytes = n_c * V * 2.0 * 2 + E * 2.0
+    out = {"metric": METRICS[5], "value": n_c / (ms / 1e3), "ms_per_step": ms, "ms_per_step_median": med,
+           "steps": steps, "warmup": warmup, "completion_tokens": n_c,
+           "step_hbm_frac": step_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+           "step_hbm_frac_median": step_bytes / (med / 1e3) / 1e9 / PEAK_HBM_GBS,
+           "kernels_ms_per_step": {k: round(v[0] / 2, 4) for k, v in kern.items()},
+           "inputs": "workload 5 shapes, mask and targets; N(0,3) bf16 logits drawn on the GPU (seeded)"}
+    for k, b in (("stream_fwd", n_c * V * 2.0), ("stream_bwd", n_c * V * 2.0 + E * 2.0)):
+        if k in kern:
+            out[k + "_GBs"] = b / (kern[k][0] / kern[k][1] / 1e3) / 1e9
+    del runner, logits
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(x, k, sample_tokens, row="main", shard_rows=None, sample_pairs=1):
@@ -496,6 +566,11 @@ def main():
                  "peaks_tflops": {"published": PEAK_BF16_TFLOPS, "unit_count": round(PEAK_BF16_TFLOPS_UNITS, 1)},
                  "kernels_ms_per_step": {k: round(v[0] / kernels_steps, 4) for k, v in kernels.items()}}
 
+    also = None
+    if a.workload == 2 and row == "main" and not a.no_also:
+        print("[bench] also: the materialised-logits path at workload 5's shape", file=sys.stderr, flush=True)
+        also = {"workload5_logits_path": also_logits_path(dev)}
+
     cpu = None
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -527,6 +602,8 @@ def main():
         "host_wall_s": t_host,
     }
     line.update(extra)
+    if also is not None:
+        line["also"] = also
     s = json.dumps(line)
     print(s, flush=True)
     if a.out:
