@@ -161,6 +161,15 @@ __device__ __forceinline__ void mask_vocab_tail(Acc& acc, int vbase, int V, int 
         if (vbase + i * FRAG + 4 * (lane >> 4) + e >= V) acc.c[i][j][e] = -INFINITY;
 }
 
+// Position-tile group width of the forward-shaped contractions.  A wide
+// group streams W_vocab from HBM once per 28 position tiles; that pays off
+// while the gathered hidden rows that the eight XCDs read at once stay in the
+// 256 MB Infinity Cache.  Past 128 MiB of hidden rows (e.g. 131,072 positions
+// at H 4,096) the narrow width bounds that set to 8 XCDs x 8 tiles x 256 rows.
+__device__ __forceinline__ int fwd_group(int n_c, int H, int gm_narrow, int gm_wide) {
+  return (size_t)n_c * H * 2 <= (size_t(128) << 20) ? gm_wide : gm_narrow;
+}
+
 template <bool ZSUM>
 __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
   int* tgt_s = (int*)g_epi;                   // 256 ints
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_gemm(FwdArgs a) {
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int n_c = a.hdr->n_c;
   Sched sc;
-  sc.init(cdiv(n_c, BM), cdiv(a.V, BN), a.gm);
+  sc.init(cdiv(n_c, BM), cdiv(a.V, BN), fwd_group(n_c, a.H, a.gm, a.gm_wide));
   const int lchunk = row_lchunk(tid);
   const int nk = a.H / BK;
   // operands of a tile: W rows n0 .. n0+255 (rows past V read as zero);
@@ -468,7 +477,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int n_c = a.hdr->n_c;
   Sched sc;
-  sc.init(cdiv(n_c, BM), a.Vp / BN, a.gm);
+  sc.init(cdiv(n_c, BM), a.Vp / BN, fwd_group(n_c, a.H, a.gm, a.gm_wide));
   const int lchunk = row_lchunk(tid);
   for (int t = sc.begin; t < sc.end; t += sc.step) {
     int mt, nt;

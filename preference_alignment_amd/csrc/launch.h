@@ -33,7 +33,8 @@ struct FwdArgs {
   const uint16_t* hidden;  // [rows*T, H]
   const uint16_t* w;       // [V, H]
   unsigned hidden_bytes;   // rows*T*H*2 (< 4 GiB)
-  int H, V, Mp, gm;
+  int H, V, Mp, gm;  // position tiles per scheduler group (narrow)
+  int gm_wide;  // the group width while the gathered hidden rows fit the cache budget
   const int* idx;
   const int* tgt_c;
   const WsHeader* hdr;
@@ -105,7 +106,8 @@ struct DProdArgs {
   const uint16_t* hidden;
   const uint16_t* w;
   unsigned hidden_bytes;  // rows*T*H*2 (< 4 GiB)
-  int H, V, Vp, Mp, gm;
+  int H, V, Vp, Mp, gm;  // position tiles per scheduler group (narrow)
+  int gm_wide;  // the group width while the gathered hidden rows fit the cache budget
   const int* idx;
   const int* tgt_c;
   const int* row_c;
