@@ -20,14 +20,11 @@ using namespace dpo;
 
 namespace {
 
-// Tile-group widths (m-tiles per group) of the persistent scheduler.  The
-// forward-shaped contractions sweep the vocabulary once per group, so W_vocab
-// (the large operand) streams from HBM once per group; the kernels take the
-// wide width while the gathered hidden rows fit their cache budget (0.2-0.3
-// ms per step faster than 8 at H 4,096 and H 2,048), the narrow one past it
-// (the wide one ran 20 % slower at 131,072 positions).
+// Tile-group widths of the persistent scheduler: position tiles per group
+// (kGroupFwd, kGroupBwd) and, for the forward-shaped contractions while the
+// gathered hidden rows fit the cache budget, vocabulary tiles per group.
 constexpr int kGroupFwd = 8;
-constexpr int kGroupFwdWide = 28;
+constexpr int kGroupFwdVocab = 4;
 constexpr int kGroupBwd = 4;
 // The dHidden contraction has few output tiles (positions x H): its K =
 // vocabulary range is split in up to this many parts, the count chosen on the
@@ -363,7 +360,7 @@ int enqueue_forward_tiles(const dpo_bf16* hidden, const dpo_bf16* w, const int32
   f.V = V;
   f.Mp = L.Mp;
   f.gm = kGroupFwd;
-  f.gm_wide = kGroupFwdWide;
+  f.gn = kGroupFwdVocab;
   f.idx = at<int>(ws, L.idx);
   f.tgt_c = at<int>(ws, L.tgt);
   f.hdr = at<WsHeader>(ws, L.hdr);
@@ -690,7 +687,7 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
     dp.Vp = Vcp;
     dp.Mp = L.Mp;
     dp.gm = kGroupFwd;
-    dp.gm_wide = kGroupFwdWide;
+    dp.gn = kGroupFwdVocab;
     dp.idx = at<int>(ws, L.idx);
     dp.tgt_c = at<int>(ws, L.tgt);
     dp.row_c = at<int>(ws, L.rowc);

@@ -407,19 +407,24 @@ __host__ __device__ inline int dh_splits(int n_c, int H, int nkt, int grid, int 
 // slab ks of the dHidden partial sums: align(n_c, BM) rows of H floats each
 __host__ __device__ inline size_t dh_slab(int n_c, int H) { return (size_t)cdiv(n_c, BM) * BM * H; }
 
-// Persistent tile scheduler.  Tiles are numbered in grouped order (GM m-tiles
-// wide, m fastest, then n) and the numbering is cut into NUM_XCD contiguous
-// parts; the blocks resident on one XCD (blockIdx % NUM_XCD) walk their part
-// together, so tiles that share operand rows run at the same time on the same
-// L2.
+// Persistent tile scheduler.  Tiles are numbered in grouped order and the
+// numbering is cut into NUM_XCD contiguous parts; the blocks resident on one
+// XCD (blockIdx % NUM_XCD) walk their part together, so tiles that share
+// operand rows run at the same time on the same L2.  Two group shapes:
+//   m-grouped (gn = 0): groups of gm m-tiles, m fastest, then n;
+//   n-grouped (gn > 0): groups of gn n-tiles, n fastest, then m.
+// With n-grouping each XCD's part is a contiguous range of n-tiles over all
+// m-tiles, so every n-side operand row is fetched from HBM by one XCD only
+// and the m-side operand must stay in the Infinity Cache.
 struct Sched {
-  int nMt, nNt, total, gm;
+  int nMt, nNt, total, gm, gn;
   int begin, end, step;
-  __device__ __forceinline__ void init(int nMt_, int nNt_, int gm_) {
+  __device__ __forceinline__ void init(int nMt_, int nNt_, int gm_, int gn_ = 0) {
     nMt = nMt_;
     nNt = nNt_;
     total = nMt * nNt;
     gm = gm_ < 1 ? 1 : gm_;
+    gn = gn_ < 0 ? 0 : gn_;
     const int xcd = blockIdx.x % NUM_XCD;
     const int q = blockIdx.x / NUM_XCD;
     const int part = cdiv(total, NUM_XCD);
@@ -428,6 +433,16 @@ struct Sched {
     end = min(total, (xcd + 1) * part);
   }
   __device__ __forceinline__ void coords(int t, int& mt, int& nt) const {
+    if (gn > 0) {
+      const int per_group = gn * nMt;
+      const int g = t / per_group;
+      const int first = g * gn;
+      const int gs = min(nNt - first, gn);
+      const int r = t - g * per_group;
+      nt = first + r % gs;
+      mt = r / gs;
+      return;
+    }
     const int per_group = gm * nNt;
     const int g = t / per_group;
     const int first = g * gm;

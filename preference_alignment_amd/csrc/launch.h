@@ -34,7 +34,7 @@ struct FwdArgs {
   const uint16_t* w;       // [V, H]
   unsigned hidden_bytes;   // rows*T*H*2 (< 4 GiB)
   int H, V, Mp, gm;  // position tiles per scheduler group (narrow)
-  int gm_wide;  // the group width while the gathered hidden rows fit the cache budget
+  int gn;  // vocabulary tiles per scheduler group while the hidden rows fit the cache budget
   const int* idx;
   const int* tgt_c;
   const WsHeader* hdr;
@@ -107,7 +107,7 @@ struct DProdArgs {
   const uint16_t* w;
   unsigned hidden_bytes;  // rows*T*H*2 (< 4 GiB)
   int H, V, Vp, Mp, gm;  // position tiles per scheduler group (narrow)
-  int gm_wide;  // the group width while the gathered hidden rows fit the cache budget
+  int gn;  // vocabulary tiles per scheduler group while the hidden rows fit the cache budget
   const int* idx;
   const int* tgt_c;
   const int* row_c;
