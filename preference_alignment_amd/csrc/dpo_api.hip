@@ -87,7 +87,7 @@ struct Layout {
   size_t hdr = 0, idx = 0, tgt = 0, rowc = 0, rowoff = 0;
   size_t part = 0, tlogit = 0, lse64 = 0, logp64 = 0, partz = 0, zsum64 = 0;
   size_t D = 0, HT = 0;
-  size_t keysA = 0, valsA = 0, keysB = 0, valsB = 0, dhpart = 0, spos = 0, sw = 0, ohcont = 0, ohhead = 0;
+  size_t keysA = 0, valsA = 0, keysB = 0, valsB = 0, dhpart = 0, ohcont = 0, ohhead = 0;
   size_t total = 0;
 #ifdef DPO_HOST_CHECKS
   // every region the layout hands out (offset, bytes), for the host-side checks
@@ -176,8 +176,6 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     // fp32 dHidden partial slabs, one per K split (at most 2 Mp x H floats in
     // all); every slice adds into them, the finish sums them
     L.dhpart = take((size_t)2 * L.Mp * H * 4);
-    L.spos = take((size_t)L.Mp * 4);
-    L.sw = take((size_t)L.Mp * 4);
     L.ohcont = take((size_t)(L.Mp / 64) * H * 4);
     L.ohhead = take((size_t)(L.Mp / 64) * H * 4);
   }
@@ -755,23 +753,21 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
   while (bits < 31 && (1 << bits) <= V) ++bits;
   SortArgs so;
   so.tgt_c = tgt_c;
-  so.idx = idx_c;
-  so.row_c = row_c;
-  so.weight = weight;
   so.hdr = hdr;
   so.V = V;
-  so.passes = (bits + 7) / 8;
+  so.passes = (bits + kSortMaxBits - 1) / kSortMaxBits;
+  so.dbits = (bits + so.passes - 1) / so.passes;
   so.keysA = at<int>(ws, L.keysA);
   so.valsA = at<int>(ws, L.valsA);
   so.keysB = at<int>(ws, L.keysB);
   so.valsB = at<int>(ws, L.valsB);
-  so.s_pos = at<int>(ws, L.spos);
-  so.s_w = at<float>(ws, L.sw);
   RUN("sort_targets", launch_sort_targets(so, st));
   OnehotDwArgs oh;
   oh.keys = (so.passes & 1) ? so.keysB : so.keysA;
-  oh.s_pos = so.s_pos;
-  oh.s_w = so.s_w;
+  oh.vals = (so.passes & 1) ? so.valsB : so.valsA;
+  oh.idx = idx_c;
+  oh.row_c = row_c;
+  oh.weight = weight;
   oh.hidden = hidden;
   oh.hdr = hdr;
   oh.H = H;

@@ -760,99 +760,152 @@ __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
 // ---------------------------------------------------------------------------
 // one-hot term of dW_vocab: positions sorted by target, then a fixed-order sum
 // ---------------------------------------------------------------------------
-// Stable LSD radix sort (8-bit digits) of the completion positions by target
-// id, in one workgroup of 16 waves.  Each wave owns a contiguous slice of the
-// input; per pass it counts its digits (LDS), the counts are scanned
-// digit-major / wave-minor, and each wave scatters its slice 64 keys at a
-// time: a key's rank among equal digits of its 64-key chunk comes from 8
-// ballots (the lanes sharing all 8 digit bits), so equal keys keep their
-// input order.  Out-of-range targets (-1) sort last.  Afterwards every sorted
-// entry gets its flat position and row weight, for k_onehot_dw.
+// Stable LSD radix sort of the completion positions by target id, in one
+// workgroup of 16 waves, in as few passes of at most 9-bit digits as cover
+// the key range (two at vocabularies up to 2^18).  Each wave owns a
+// contiguous slice of the input; per pass it counts its digits (LDS), the
+// counts are scanned digit-major / wave-minor (one thread per digit over the
+// waves, then one wave's prefix sum over the digits), and each wave scatters
+// its slice 64 keys at a time: a key's rank among equal digits of its 64-key
+// chunk comes from one ballot per digit bit (the lanes sharing all its digit
+// bits), so equal keys keep their input order.  Out-of-range targets (-1)
+// sort last.  The payload is the compact index of each position.
 constexpr int kSortWaves = kSortThreads / 64;
+constexpr int kSortMaxDigits = 1 << kSortMaxBits;
+constexpr int kSortBatch = 8;  // 64-key chunks whose loads are in flight together
 
-// the first pass reads the raw targets: ids outside [0, V) (out of range, or
-// held by another vocabulary shard) become V, so they sort after every valid id
+// Lanes of the wave whose (valid) digit equals this lane's: one ballot per
+// digit bit.
+__device__ __forceinline__ unsigned long long digit_peers(int d, bool valid, int dbits) {
+  const unsigned long long vmask = __ballot(valid);
+  unsigned long long peers = vmask;
+#pragma unroll
+  for (int bit = 0; bit < kSortMaxBits; ++bit) {
+    if (bit < dbits) {
+      const bool set = (d >> bit) & 1;
+      const unsigned long long bb = __ballot(valid && set);
+      peers &= set ? bb : (vmask & ~bb);
+    }
+  }
+  return peers;
+}
+
+// pass 0 reads the targets and maps the ones outside [0, V) to V
 __device__ __forceinline__ int sort_key(const int* kin, int i, int pass, int V) {
   const int k = kin[i];
   return (pass > 0 || ((unsigned)k < (unsigned)V)) ? k : V;
 }
 
 __global__ __launch_bounds__(kSortThreads) void k_sort_targets(SortArgs a) {
-  __shared__ int cnt[kSortWaves][256];
-  __shared__ int dig_base[256];
+  __shared__ int cnt[kSortWaves][kSortMaxDigits];
+  __shared__ int dig_tot[kSortMaxDigits];
+  __shared__ int dig_base[kSortMaxDigits];
   const int n = a.hdr->n_c;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int per = cdiv(n, kSortWaves);
   const int lo = min(n, per * wave), hi = min(n, lo + per);
   const unsigned long long below = (1ull << lane) - 1ull;
+  const int nd = 1 << a.dbits;
+  const unsigned dmask = (unsigned)nd - 1u;
   const int* kin = a.tgt_c;
   const int* vin = nullptr;
   int* kout = a.keysB;
   int* vout = a.valsB;
   for (int p = 0; p < a.passes; ++p) {
-    const int shift = 8 * p;
-#pragma unroll
-    for (int d = lane; d < 256; d += 64) cnt[wave][d] = 0;
+    const int shift = a.dbits * p;
+    for (int d = lane; d < nd; d += 64) cnt[wave][d] = 0;
     __syncthreads();
-    for (int base = lo; base < hi; base += 64) {
-      const int i = base + lane;
-      if (i < hi) atomicAdd(&cnt[wave][((unsigned)sort_key(kin, i, p, a.V) >> shift) & 255u], 1);
+    // keys are loaded kSortBatch chunks at a time, so one load latency
+    // serves several chunks
+    for (int base = lo; base < hi; base += 64 * kSortBatch) {
+      int kk[kSortBatch];
+#pragma unroll
+      for (int j = 0; j < kSortBatch; ++j) {
+        const int i = base + 64 * j + lane;
+        kk[j] = i < hi ? sort_key(kin, i, p, a.V) : -1;
+      }
+      // one LDS add per distinct digit of a chunk (the lowest lane of each
+      // group of equal digits): skewed targets would serialise per-key atomics
+#pragma unroll
+      for (int j = 0; j < kSortBatch; ++j) {
+        if (base + 64 * j >= hi) break;
+        const bool valid = kk[j] >= 0;
+        const int d = (int)(((unsigned)kk[j] >> shift) & dmask);
+        const unsigned long long peers = digit_peers(d, valid, a.dbits);
+        if (valid && __popcll(peers & below) == 0) cnt[wave][d] += __popcll(peers);
+        __builtin_amdgcn_wave_barrier();
+      }
     }
     __syncthreads();
-    if (tid < 256) {
+    for (int d = tid; d < nd; d += kSortThreads) {
       int run = 0;
       for (int w = 0; w < kSortWaves; ++w) {
-        const int c = cnt[w][tid];
-        cnt[w][tid] = run;
+        const int c = cnt[w][d];
+        cnt[w][d] = run;
         run += c;
       }
-      dig_base[tid] = run;  // digit total for now
+      dig_tot[d] = run;
     }
     __syncthreads();
-    if (tid == 0) {
-      int run = 0;
-      for (int d = 0; d < 256; ++d) {
-        const int c = dig_base[d];
-        dig_base[d] = run;
-        run += c;
-      }
-    }
-    __syncthreads();
-    for (int base = lo; base < hi; base += 64) {
-      const int i = base + lane;
-      const bool valid = i < hi;
-      const int k = valid ? sort_key(kin, i, p, a.V) : 0;
-      const int d = ((unsigned)k >> shift) & 255u;
-      const unsigned long long vmask = __ballot(valid);
-      unsigned long long peers = vmask;
+    if (wave == 0) {
+      // lane l holds digits 8 l .. 8 l + 7: exclusive prefix sum over digits
+      constexpr int kPer = kSortMaxDigits / 64;
+      int v[kPer];
+      int s = 0;
 #pragma unroll
-      for (int bit = 0; bit < 8; ++bit) {
-        const bool set = (d >> bit) & 1;
-        const unsigned long long bb = __ballot(valid && set);
-        peers &= set ? bb : (vmask & ~bb);
+      for (int j = 0; j < kPer; ++j) {
+        const int d = kPer * lane + j;
+        v[j] = d < nd ? dig_tot[d] : 0;
+        s += v[j];
       }
-      const int rank = __popcll(peers & below);
-      const int slot = valid ? dig_base[d] + cnt[wave][d] + rank : 0;
-      __builtin_amdgcn_wave_barrier();
-      if (valid) {
-        kout[slot] = k;
-        vout[slot] = vin ? vin[i] : i;
-        if (rank == 0) cnt[wave][d] += __popcll(peers);
+      int inc = s;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += y;
       }
-      __builtin_amdgcn_wave_barrier();
+      int run = inc - s;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int d = kPer * lane + j;
+        if (d < nd) dig_base[d] = run;
+        run += v[j];
+      }
+    }
+    __syncthreads();
+    for (int base = lo; base < hi; base += 64 * kSortBatch) {
+      int kk[kSortBatch], vv[kSortBatch];
+#pragma unroll
+      for (int j = 0; j < kSortBatch; ++j) {
+        const int i = base + 64 * j + lane;
+        kk[j] = i < hi ? sort_key(kin, i, p, a.V) : 0;
+        vv[j] = i < hi ? (vin ? vin[i] : i) : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kSortBatch; ++j) {
+        if (base + 64 * j >= hi) break;
+        const int i = base + 64 * j + lane;
+        const bool valid = i < hi;
+        const int k = kk[j];
+        const int d = (int)(((unsigned)k >> shift) & dmask);
+        const unsigned long long peers = digit_peers(d, valid, a.dbits);
+        const int rank = __popcll(peers & below);
+        const int slot = valid ? dig_base[d] + cnt[wave][d] + rank : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+          kout[slot] = k;
+          vout[slot] = vv[j];
+          if (rank == 0) cnt[wave][d] += __popcll(peers);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
     }
     __syncthreads();
     kin = kout;
     vin = vout;
     kout = (kout == a.keysB) ? a.keysA : a.keysB;
     vout = (vout == a.valsB) ? a.valsA : a.valsB;
-  }
-  // per sorted entry: flat position and row weight, read by k_onehot_dw
-  for (int i = tid; i < n; i += kSortThreads) {
-    const int m = vin[i];
-    a.s_pos[i] = a.idx[m];
-    a.s_w[i] = a.weight[a.row_c[m]];
   }
 }
 
@@ -897,8 +950,10 @@ __global__ __launch_bounds__(256) void k_onehot_dw(OnehotDwArgs a) {
     key_s[tid] = (i >= 0 && i < n) ? a.keys[i] : -2;
   }
   if (tid < kOnehotChunk) {
-    pos_s[tid] = tid < m ? a.s_pos[i0 + tid] : 0;
-    w_s[tid] = tid < m ? a.s_w[i0 + tid] : 0.f;
+    // flat position and row weight of each sorted entry
+    const int c = tid < m ? a.vals[i0 + tid] : 0;
+    pos_s[tid] = tid < m ? a.idx[c] : 0;
+    w_s[tid] = tid < m ? a.weight[a.row_c[c]] : 0.f;
   }
   __syncthreads();
   const int c0 = blockIdx.y * kOnehotCols + tid * 4;

@@ -144,24 +144,22 @@ struct DhFinishArgs {
 
 struct SortArgs {
   const int* tgt_c;     // [n_c] keys in position order
-  const int* idx;
-  const int* row_c;
-  const float* weight;  // [rows]
   const WsHeader* hdr;
   int V;                // keys outside [0, V) sort last, as V
-  int passes;           // 8-bit digits needed to cover V
+  int passes;           // radix passes covering keys 0..V
+  int dbits;            // digit bits per pass (at most kSortMaxBits)
   int* keysA;
   int* valsA;
   int* keysB;
   int* valsB;
-  int* s_pos;           // [n_c] flat position of each sorted entry
-  float* s_w;           // [n_c] its row weight
 };
 
 struct OnehotDwArgs {
   const int* keys;      // [n_c] targets, sorted
-  const int* s_pos;     // [n_c] flat positions, ascending within a target
-  const float* s_w;     // [n_c] row weights
+  const int* vals;      // [n_c] compact indices, ascending within a target
+  const int* idx;       // [n_c] flat position of each compact index
+  const int* row_c;     // [n_c] row of each compact index
+  const float* weight;  // [rows]
   const uint16_t* hidden;
   const WsHeader* hdr;
   int H, V;
@@ -248,6 +246,7 @@ hipError_t launch_zero_rows(const ZeroRowsArgs& a, long positions, hipStream_t s
 hipError_t launch_sort_targets(const SortArgs& a, hipStream_t s);
 hipError_t launch_onehot_dw(const OnehotDwArgs& a, int Mp, hipStream_t s);
 constexpr int kSortThreads = 1024;
+constexpr int kSortMaxBits = 9;
 hipError_t launch_stream_fwd(const StreamFwdArgs& a, long positions, hipStream_t s);
 hipError_t launch_stream_row_sums(const StreamRowSumArgs& a, hipStream_t s);
 hipError_t launch_stream_bwd(const StreamBwdArgs& a, long positions, int grid, hipStream_t s);

@@ -67,9 +67,9 @@ static void check_layout(int op, int rows, int T, int H, int V) {
   CHECK(Mp * Vcp * 2 <= kChunkBytes || L.chunk_tiles == 1);
   // Hc^T: H rows of ldt positions; the gather writes positions < align(n_c, 256) <= Mp < ldt
   CHECK((size_t)L.ldt > Mp && region_bytes(L, L.HT) >= (size_t)H * L.ldt * 2);
-  // radix sort buffers and the sorted entries: n_c <= Mp each
-  CHECK(region_bytes(L, L.keysA) >= Mp * 4 && region_bytes(L, L.valsB) >= Mp * 4);
-  CHECK(region_bytes(L, L.spos) >= Mp * 4 && region_bytes(L, L.sw) >= Mp * 4);
+  // radix sort buffers: n_c <= Mp keys and values each
+  CHECK(region_bytes(L, L.keysA) >= Mp * 4 && region_bytes(L, L.valsA) >= Mp * 4);
+  CHECK(region_bytes(L, L.keysB) >= Mp * 4 && region_bytes(L, L.valsB) >= Mp * 4);
   // one-hot run pieces: one H-float row per 64-entry chunk, cdiv(n_c, 64) <= Mp / 64
   CHECK(region_bytes(L, L.ohcont) >= (Mp / 64) * H * 4 && region_bytes(L, L.ohhead) >= (Mp / 64) * H * 4);
   // dHidden slabs: for every completion count the device may meet, splits x
