@@ -377,21 +377,45 @@ __global__ __launch_bounds__(256) void k_row_sums(RowSumArgs a) {
 // vocabulary shards: a shard's (max, sum exp, target logit) per position, and
 // the combine of S shards' values into the whole-vocabulary lse and log p
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_shard_partials(ShardPartialArgs a) {
-  const int m = blockIdx.x * 256 + threadIdx.x;
-  if (m >= a.hdr->n_c) return;
+// Laid out like k_combine: 16 positions per block, the shard's vocabulary
+// tiles split over 16 thread groups (tile j to group j % 16), the groups'
+// fp64 shares added in group order.
+__global__ __launch_bounds__(kCombPos * kCombGroups) void k_shard_partials(ShardPartialArgs a) {
+  __shared__ float red_m[kCombGroups][kCombPos];
+  __shared__ double red_s[kCombGroups][kCombPos];
+  const int p = threadIdx.x % kCombPos, g = threadIdx.x / kCombPos;
+  const int m = blockIdx.x * kCombPos + p;
+  const int n_c = a.hdr->n_c;
+  if (blockIdx.x * kCombPos >= n_c) return;
+  const bool live = m < n_c;
   float M = -INFINITY;
-  for (int j = 0; j < a.nVt; ++j) M = fmaxf(M, a.part[(size_t)j * a.Mp + m].x);
-  double S = 0.0;
-  const float Ml = M * kLog2e;
-  for (int j = 0; j < a.nVt; ++j) {
-    const float2 t = a.part[(size_t)j * a.Mp + m];
-    S += (double)(t.y * fast_exp2(fmaf(t.x, kLog2e, -Ml)));
+  if (live) {
+#pragma unroll 4
+    for (int j = g; j < a.nVt; j += kCombGroups) M = fmaxf(M, a.part[(size_t)j * a.Mp + m].x);
   }
-  const int p = a.idx[m];
-  a.out_max[p] = M;
-  a.out_sum[p] = (float)S;
-  a.out_tgt[p] = a.tgt_c[m] >= 0 ? a.tgt_logit[m] : -INFINITY;
+  red_m[g][p] = M;
+  __syncthreads();
+  M = red_m[0][p];
+  for (int q = 1; q < kCombGroups; ++q) M = fmaxf(M, red_m[q][p]);
+  double S = 0.0;
+  if (live) {
+    const float Ml = M * kLog2e;
+#pragma unroll 4
+    for (int j = g; j < a.nVt; j += kCombGroups) {
+      const float2 t = a.part[(size_t)j * a.Mp + m];
+      S += (double)(t.y * fast_exp2(fmaf(t.x, kLog2e, -Ml)));
+    }
+  }
+  red_s[g][p] = S;
+  __syncthreads();
+  if (g == 0 && live) {
+    S = red_s[0][p];
+    for (int q = 1; q < kCombGroups; ++q) S += red_s[q][p];
+    const int pos = a.idx[m];
+    a.out_max[pos] = M;
+    a.out_sum[pos] = (float)S;
+    a.out_tgt[pos] = a.tgt_c[m] >= 0 ? a.tgt_logit[m] : -INFINITY;
+  }
 }
 
 __global__ __launch_bounds__(256) void k_shard_combine(ShardCombineArgs a) {
@@ -1091,7 +1115,7 @@ hipError_t launch_fwd_gemm(const FwdArgs& a, int grid, hipStream_t s) {
 }
 
 hipError_t launch_shard_partials(const ShardPartialArgs& a, int Mp, hipStream_t s) {
-  hipLaunchKernelGGL(k_shard_partials, dim3(Mp / 256), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_shard_partials, dim3(Mp / kCombPos), dim3(kCombPos * kCombGroups), 0, s, a);
   return hipGetLastError();
 }
 
