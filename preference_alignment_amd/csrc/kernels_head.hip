@@ -47,12 +47,15 @@ using namespace gemm;
 constexpr int kCompactThreads = 1024;
 constexpr int kCompactWaves = kCompactThreads / 64;
 
-// One workgroup walks the positions in rounds of 1,024 consecutive ones
-// (thread t takes position 1024 r + t, so loads and stores are coalesced).
-// A position's output slot is the running count of earlier rounds plus the
-// count of earlier waves in its round (a 16-entry LDS table, double buffered
-// so each round needs one barrier) plus its rank among the wave's set mask
-// lanes (a ballot).  Row-major ascending order falls out of this directly.
+// One workgroup walks the positions in rounds of 4,096 consecutive ones,
+// thread t taking positions 4096 r + 4 t .. + 3.  A position's output slot is
+// the running count of earlier rounds plus the count of earlier waves in its
+// round (a 16-entry LDS table, double buffered so each round needs one
+// barrier) plus the count of earlier lanes of its wave (a prefix sum over the
+// lanes' counts) plus that of its thread's earlier positions.  Row-major
+// ascending order falls out of this directly.
+constexpr int kCompactPer = 4;  // positions per thread and round
+
 __global__ __launch_bounds__(kCompactThreads) void k_compact(CompactArgs a) {
   __shared__ int wtot[2][kCompactWaves];
   __shared__ int err;
@@ -60,45 +63,61 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CompactArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const long N = (long)a.rows * a.T;
   if (tid == 0) err = 0;
-  const unsigned long long lt_mask = (1ull << lane) - 1ull;
   int base = 0;  // completion positions before this round
   int bad = 0;
-  for (long r0 = 0, round = 0; r0 < N; r0 += kCompactThreads, ++round) {
-    const long p = r0 + tid;
-    const bool in = p < N;
-    const bool on = in && a.mask[p] != 0;
-    const unsigned long long bal = __ballot(on);
+  constexpr int kRound = kCompactThreads * kCompactPer;
+  for (long r0 = 0, round = 0; r0 < N; r0 += kRound, ++round) {
+    const long p0 = r0 + (long)kCompactPer * tid;
+    bool on[kCompactPer];
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < kCompactPer; ++u) {
+      on[u] = p0 + u < N && a.mask[p0 + u] != 0;
+      c += on[u];
+    }
+    // inclusive prefix sum of the lanes' counts
+    int inc = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += y;
+    }
     const int buf = (int)(round & 1);
-    if (lane == 0) wtot[buf][wave] = __popcll(bal);
+    if (lane == 63) wtot[buf][wave] = inc;
     __syncthreads();
     int before = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < kCompactWaves; ++w) {
-      const int c = wtot[buf][w];
-      before += w < wave ? c : 0;
-      total += c;
+      const int cw = wtot[buf][w];
+      before += w < wave ? cw : 0;
+      total += cw;
     }
-    const int pos = base + before + __popcll(bal & lt_mask);
-    if (in) {
-      if (p % a.T == 0) a.row_off[p / a.T] = pos;
-      if (on) {
-        int t = a.targets[p];
-        if (t < 0 || t >= a.V_total) {
-          bad = 1;
-          t = -1;
+    int pos = base + before + inc - c;
+#pragma unroll
+    for (int u = 0; u < kCompactPer; ++u) {
+      const long p = p0 + u;
+      if (p < N) {
+        if (p % a.T == 0) a.row_off[p / a.T] = pos;
+        if (on[u]) {
+          int t = a.targets[p];
+          if (t < 0 || t >= a.V_total) {
+            bad = 1;
+            t = -1;
+          } else {
+            t -= a.v_begin;
+            if (t < 0 || t >= a.V) t = -1;  // held by another vocabulary shard
+          }
+          a.idx[pos] = (int)p;
+          a.tgt_c[pos] = t;
+          a.row_c[pos] = (int)(p / a.T);
+          ++pos;
         } else {
-          t -= a.v_begin;
-          if (t < 0 || t >= a.V) t = -1;  // held by another vocabulary shard
-        }
-        a.idx[pos] = (int)p;
-        a.tgt_c[pos] = t;
-        a.row_c[pos] = (int)(p / a.T);
-      } else {
-        if (a.lse_out) a.lse_out[p] = 0.f;
-        if (a.off_max) {
-          a.off_max[p] = -INFINITY;
-          a.off_sum[p] = 0.f;
-          a.off_tgt[p] = -INFINITY;
+          if (a.lse_out) a.lse_out[p] = 0.f;
+          if (a.off_max) {
+            a.off_max[p] = -INFINITY;
+            a.off_sum[p] = 0.f;
+            a.off_tgt[p] = -INFINITY;
+          }
         }
       }
     }
