@@ -46,6 +46,10 @@ CASES = {
     # vocabulary tile + 8 rows, the smallest overhang V % 8 == 0 allows),
     # H = 128 (two K stages)
     "tile_plus": lambda: _case("tile_plus", seed=108, rows=2, T=160, H=128, V=264, prompt_lo=31, prompt_hi=31),
+    # V = 200,000 needs 18 key bits: the target sort runs two passes of 9-bit
+    # digits, on Zipf targets (long runs of equal digits); every dW row checked
+    "wide_vocab_sort": lambda: _case("wide_vocab_sort", seed=109, rows=4, T=160, H=64, V=200000, prompt_lo=16,
+                                     prompt_hi=64, w_std=0.25, targets_dist="zipf"),
     # minimum sizes
     "tiny_min": lambda: _case("tiny_min", seed=104, rows=2, T=3, H=64, V=8, prompt_lo=0, prompt_hi=1,
                               w_std=0.3),
@@ -147,7 +151,7 @@ def test_accumulate_dw_adds(case):
     assert float((dw2 - 2 * dw1).abs().max()) <= 1e-6 * float(dw1.abs().max())
 
 
-@pytest.mark.parametrize("case", ["ragged_medium", "two_vocab_slices"])
+@pytest.mark.parametrize("case", ["ragged_medium", "two_vocab_slices", "wide_vocab_sort"])
 def test_run_to_run_bitwise_deterministic(case):
     dev = need_gpu()
     x = CASES[case]()
