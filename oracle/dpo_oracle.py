@@ -29,7 +29,7 @@ changelog and section "Why the reference is scored offline": chosen and
 rejected rows of a pair sit next to each other; reference scores are plain
 per-row sums with no beta.
 
-Readings taken where the pages leave a step open (all listed in the design doc):
+Readings taken where the pages leave a step open:
 targets arrive already shifted (targets[r, t] is the token predicted from
 hidden[r, t]); an explicit 0/1 mask selects completion positions and targets
 at mask-0 positions are never read; accuracy uses a strict ``>``; the
