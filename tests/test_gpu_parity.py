@@ -261,3 +261,40 @@ def test_validation_errors_raise():
     with pytest.raises(ValueError):
         D.dpo_seq_logps(d["hidden"], d["w"], d["targets"], d["mask"],
                         torch.empty(2, dtype=torch.float32, device=dev), workspace=small)
+
+
+def test_backward_ordered_on_a_user_stream_and_replayable_in_a_graph():
+    # every launch of the call goes on the caller's stream: work enqueued on
+    # that stream right after the call sees the finished gradients, and a
+    # call captured in a graph replays to the eager result (the path issues
+    # no memset and no allocation)
+    dev = need_gpu()
+    x = CASES["ragged_medium"]()
+    d = dev_inputs(x, dev)
+    g = run_forward(x, d, dev)
+    weight = torch.linspace(-0.05, 0.05, x.rows, dtype=torch.float32, device=dev)
+    dh_ref, dw_ref = run_backward(x, d, g["lse"], weight, dev)
+    R, T = x.rows, x.T
+    ws = D.alloc_workspace(D.DPO_OP_HEAD_BACKWARD, R, T, x.H, x.V, dev)
+    dh = torch.full((R, T, x.H), float("nan"), dtype=torch.float32, device=dev)
+    dw = torch.full((x.V, x.H), float("nan"), dtype=torch.float32, device=dev)
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        D.dpo_head_backward(d["hidden"], d["w"], d["targets"], d["mask"], g["lse"], weight, dh, dw, 0,
+                            workspace=ws)
+        snap_h, snap_w = dh.clone(), dw.clone()
+    torch.cuda.synchronize()
+    assert torch.equal(snap_h, dh_ref) and torch.equal(snap_w, dw_ref)
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        D.dpo_head_backward(d["hidden"], d["w"], d["targets"], d["mask"], g["lse"], weight, dh, dw, 0,
+                            workspace=ws)
+    for _ in range(3):
+        dh.fill_(float("nan"))
+        dw.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dh, dh_ref) and torch.equal(dw, dw_ref)
