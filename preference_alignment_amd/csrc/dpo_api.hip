@@ -33,12 +33,13 @@ constexpr int kGroupBwd = 4;
 // and every vocabulary slice adds into the same slabs.
 constexpr int kMaxSplitDh = 4;
 // The backward holds the bf16 softmax part of dlogits (D) only for one slice
-// of the vocabulary at a time: D stays under this many bytes (balanced slices
-// of whole 256-wide tiles).
+// of the vocabulary at a time: D's columns stay under this many bytes
+// (balanced slices of whole 256-wide tiles; each D row carries a 128-byte pad).
 constexpr size_t kChunkBytes = size_t(2) << 30;
 // output tiles one round of the persistent contractions covers (one per CU of MI355X)
 constexpr int kRoundTiles = 256;
 constexpr int kTransPad = 64;  // elements
+constexpr int kDPad = 64;      // elements: D rows 128 bytes off a power-of-two stride
 // workgroups per CU of the chunked streaming backward
 constexpr int kStreamBwdBlocksPerCU = 32;
 
@@ -82,6 +83,7 @@ struct Layout {
   int Vp = 0;   // vocabulary rounded up to the GEMM tile
   int nVt = 0;  // vocabulary tiles of the forward contraction
   int chunk_tiles = 0;  // vocabulary tiles per backward slice
+  int ldd = 0;          // D row stride (elements)
   int n_chunks = 0;
   int ldt = 0;  // row stride (elements) of Hc^T: positions plus a pad
   size_t hdr = 0, idx = 0, tgt = 0, rowc = 0, rowoff = 0;
@@ -167,7 +169,10 @@ Layout make_layout(int op, int rows, int T, int H, int V) {
     // a power of two (2^15 bytes at 16,384 positions), where all rows of a
     // tile would fall on the same HBM channels
     L.ldt = L.Mp + kTransPad;
-    L.D = take((size_t)L.Mp * Vcp * 2);
+    // D rows: a pad of 128 bytes keeps their stride off a power of two
+    // (131,072 bytes at 256 tiles), as for Hc^T below
+    L.ldd = Vcp + kDPad;
+    L.D = take((size_t)L.Mp * L.ldd * 2);
     L.HT = take((size_t)H * L.ldt * 2);
     L.keysA = take((size_t)L.Mp * 4);
     L.valsA = take((size_t)L.Mp * 4);
@@ -189,7 +194,7 @@ bool backward_addressable(int op, int rows, int T, int H, int V) {
   if (op != DPO_OP_HEAD_BACKWARD) return true;
   const Layout L = make_layout(op, rows, T, H, V);
   const size_t vc = (size_t)L.chunk_tiles * gemm::BN;
-  return (size_t)L.Mp * vc * 2 < (size_t(1) << 32) && vc * (size_t)H * 2 < (size_t(1) << 32);
+  return (size_t)L.Mp * L.ldd * 2 < (size_t(1) << 32) && vc * (size_t)H * 2 < (size_t(1) << 32);
 }
 
 template <typename T>
@@ -683,6 +688,7 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
     dp.H = H;
     dp.V = Vc;
     dp.Vp = Vcp;
+    dp.ldd = L.ldd;
     dp.Mp = L.Mp;
     dp.gm = kGroupFwd;
     dp.gn = kGroupFwdVocab;
@@ -701,6 +707,7 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
     dh.H = H;
     dh.V = Vc;
     dh.Vp = Vcp;
+    dh.ldd = L.ldd;
     dh.Mp = L.Mp;
     dh.gm = kGroupBwd;
     dh.max_split = kMaxSplitDh;
@@ -716,6 +723,7 @@ int enqueue_head_backward(const dpo_bf16* hidden, const dpo_bf16* w_vocab, const
     dw.V = Vc;
     dw.H = H;
     dw.Vp = Vcp;
+    dw.ldd = L.ldd;
     dw.Mp = L.Mp;
     dw.ldt = L.ldt;
     dw.gm = kGroupBwd;

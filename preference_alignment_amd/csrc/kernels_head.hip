@@ -577,7 +577,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dprod_gemm(DProdArgs a) {
       const int g = it * NTHREADS + etid;
       const int p = g >> 5, c = g & 31;
       const u32x4 v = *(const u32x4*)stage_at(p, c * 8);
-      __builtin_nontemporal_store(v, (u32x4*)(a.D + (size_t)(m0 + p) * a.Vp + n0 + c * 8));
+      __builtin_nontemporal_store(v, (u32x4*)(a.D + (size_t)(m0 + p) * a.ldd + n0 + c * 8));
     }
     __syncthreads();
   }
@@ -677,7 +677,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dh_gemm(DhArgs a) {
     const int m0 = mt * BM, n0 = nt * BN;
     const int kb = ks * nks;
     const int nk = max(0, min(nks, nkt - kb));
-    const RowOperand dop = row_operand(a.D + (size_t)m0 * a.Vp, a.Vp, (long)a.Mp - m0, kb * BK, tid);
+    const RowOperand dop = row_operand(a.D + (size_t)m0 * a.ldd, a.ldd, (long)a.Mp - m0, kb * BK, tid);
     const KOperand wop = kmajor_operand(a.w + (size_t)kb * BK * a.H + n0, a.H, (long)a.V - kb * BK, tid);
     Acc acc;
     mainloop(acc, dop, wop, nk, wave, lane, wm, wn);
@@ -793,7 +793,7 @@ __global__ __launch_bounds__(NTHREADS) void k_dw_gemm(DwArgs a) {
     sc.coords(t, mt, nt);
     const int h0 = mt * BM, v0 = nt * BN;
     const RowOperand hop = row_operand(a.ht + (size_t)h0 * a.ldt, a.ldt, (long)a.H - h0, 0, tid);
-    const KOperand dop = kmajor_operand(a.D + v0, a.Vp, (long)align_up((size_t)n_c, BM), tid);
+    const KOperand dop = kmajor_operand(a.D + v0, a.ldd, (long)align_up((size_t)n_c, BM), tid);
     Acc acc;
     mainloop(acc, hop, dop, nk, wave, lane, wm, wn);
     dwt_store_tile(acc, a.d_w, h0, v0, a.V, a.H, a.accumulate, opaque(tid), opaque(lane), wm, wn);

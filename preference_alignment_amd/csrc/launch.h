@@ -103,6 +103,7 @@ struct GatherHTArgs {
 };
 
 struct DProdArgs {
+  int ldd;  // D row stride (elements)
   const uint16_t* hidden;
   const uint16_t* w;
   unsigned hidden_bytes;  // rows*T*H*2 (< 4 GiB)
@@ -118,6 +119,7 @@ struct DProdArgs {
 };
 
 struct DhArgs {
+  int ldd;  // D row stride (elements)
   const uint16_t* D;    // [Mp, Vp] the slice's D
   const uint16_t* w;    // [V, H] the slice's rows of W_vocab, read K-major (K = vocabulary)
   int H, V, Vp, Mp, gm;
@@ -169,6 +171,7 @@ struct OnehotDwArgs {
 };
 
 struct DwArgs {
+  int ldd;  // D row stride (elements)
   const uint16_t* D;    // [Mp, Vp] the slice's D, read K-major (K = positions)
   const uint16_t* ht;   // [H, ldt]
   int V, H, Vp, Mp, ldt, gm, accumulate;

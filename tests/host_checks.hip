@@ -63,7 +63,7 @@ static void check_layout(int op, int rows, int T, int H, int V) {
   CHECK(L.chunk_tiles >= 1 && L.n_chunks == cdiv(L.nVt, L.chunk_tiles));
   CHECK((long long)(L.n_chunks - 1) * L.chunk_tiles < L.nVt);
   const size_t Vcp = (size_t)L.chunk_tiles * gemm::BN;
-  CHECK(region_bytes(L, L.D) >= Mp * Vcp * 2);
+  CHECK((size_t)L.ldd >= Vcp && region_bytes(L, L.D) >= Mp * (size_t)L.ldd * 2);
   CHECK(Mp * Vcp * 2 <= kChunkBytes || L.chunk_tiles == 1);
   // Hc^T: H rows of ldt positions; the gather writes positions < align(n_c, 256) <= Mp < ldt
   CHECK((size_t)L.ldt > Mp && region_bytes(L, L.HT) >= (size_t)H * L.ldt * 2);

@@ -57,12 +57,12 @@ def test_workspace_sizes(L):
     Mp, Vcp, ldt, H = 16384, 65536, 16448, 4096
     parts = [256,                      # header
              3 * Mp * 4, 256,          # idx, targets, rows; row offsets (256-byte aligned)
-             Mp * Vcp * 2,             # D of one slice
+             Mp * (Vcp + 64) * 2,      # D of one slice (rows padded 128 bytes)
              H * ldt * 2,              # Hc^T
              4 * Mp * 4,               # radix sort keys / values
              2 * Mp * H * 4,           # dHidden partial slabs (at most 2 Mp x H floats)
              2 * (Mp // 64) * H * 4]   # one-hot run pieces
-    assert bw == sum(parts) == 2_827_944_448
+    assert bw == sum(parts) == 2_830_041_600
     assert bw <= 4.5e9
     # a slice of D or of W past 4 GiB is refused (32-bit offsets)
     assert D.dpo_workspace_bytes(D.DPO_OP_HEAD_BACKWARD, 2, 1 << 22, 64, 1024) == 0
