@@ -215,7 +215,9 @@ int persistent_grid() {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cus[dev] = n;
+    // the tile scheduler cuts the tiles into one part per XCD (blockIdx % 8):
+    // a grid of fewer than 8 blocks would leave parts unvisited
+    cus[dev] = std::max(n, gemm::NUM_XCD);
   }
   return cus[dev];
 }
