@@ -298,3 +298,53 @@ def test_backward_ordered_on_a_user_stream_and_replayable_in_a_graph():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(dh, dh_ref) and torch.equal(dw, dw_ref)
+
+
+def test_whole_step_replays_in_a_graph():
+    # forward, loss and backward captured together replay to the eager results
+    # (the timing events are off; no launch of the path allocates or memsets)
+    dev = need_gpu()
+    x = CASES["ragged_small"]()
+    d = dev_inputs(x, dev)
+    R, T = x.rows, x.T
+    g = run_forward(x, d, dev)
+    ref = (g["logp_sum64"] + torch.from_numpy(x.ref_noise).to(dev)).float()
+    gl = run_loss(g["logp_sum64"], ref, x.beta, x.layout, dev)
+    dh_ref, dw_ref = run_backward(x, d, g["lse"], gl["weight"], dev)
+    eager = [g["logp_sum64"].clone(), g["lse"].clone(), gl["loss"].clone(), gl["weight"].clone(), dh_ref, dw_ref]
+
+    ws_f = D.alloc_workspace(D.DPO_OP_SEQ_LOGPS, R, T, x.H, x.V, dev)
+    ws_b = D.alloc_workspace(D.DPO_OP_HEAD_BACKWARD, R, T, x.H, x.V, dev)
+    s32 = torch.empty(R, dtype=torch.float32, device=dev)
+    s64 = torch.empty(R, dtype=torch.float64, device=dev)
+    lse = torch.empty(R, T, dtype=torch.float32, device=dev)
+    ntok = torch.empty(R, dtype=torch.int32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    weight = torch.empty(R, dtype=torch.float32, device=dev)
+    reward = torch.empty(R, dtype=torch.float32, device=dev)
+    margin = torch.empty(R // 2, dtype=torch.float32, device=dev)
+    acc = torch.empty(1, dtype=torch.float32, device=dev)
+    dh = torch.empty(R, T, x.H, dtype=torch.float32, device=dev)
+    dw = torch.empty(x.V, x.H, dtype=torch.float32, device=dev)
+
+    def step():
+        D.dpo_seq_logps(d["hidden"], d["w"], d["targets"], d["mask"], s32, s64, lse, ntok, workspace=ws_f)
+        D.dpo_loss(s64, ref, x.beta, x.layout, loss, weight, reward, margin, acc)
+        D.dpo_head_backward(d["hidden"], d["w"], d["targets"], d["mask"], lse, weight, dh, dw, 0, workspace=ws_b)
+
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        step()  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step()
+    for _ in range(3):
+        for t in (s64, lse, loss, weight, dh, dw):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((s64, lse, loss, weight, dh, dw), eager):
+            assert torch.equal(got, want)
